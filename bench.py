@@ -1,0 +1,209 @@
+"""Throughput of the DeepSeekMoE layer forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one full layer forward (router, dispatch, grouped SwiGLU expert
+GEMMs with the shared experts in the same launches, combine) over one batch
+of seeded synthetic hidden states, with every input already resident in HBM.
+The default workload is the 16B-model-shaped prefill layer in bfloat16
+(T=8192 tokens, d=2048, 64 routed + 2 shared experts, top-6, intermediate
+1408).  The decode-shaped batch (T=64, same layer) is timed beside it.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (MFMA / vector)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="moe16b_prefill_bf16")
+    ap.add_argument("--decode-workload", default="moe16b_decode_bf16")
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    return ap.parse_args()
+
+
+def upload(inp, device):
+    import numpy as np
+    import torch
+
+    def dev(raw):
+        t = torch.from_numpy(np.ascontiguousarray(raw))
+        if inp.w.dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(device)
+
+    w = inp.w
+    b = inp.gate_bias()
+    return dict(u=dev(inp.u_raw()), E=dev(inp.E_gate_raw()), Wr=dev(inp.routed_all_raw(threads=16)),
+                Ws=dev(inp.shared_all_raw()) if w.K_s else None,
+                bias=None if b is None else torch.from_numpy(b).to(device))
+
+
+def time_layer(mx, t, w, steps, warmup, stage_timing):
+    """Warm up, then time exactly `steps` forwards between two synchronisations."""
+    import torch
+
+    I = t["Wr"].numel() // (3 * w.N * w.d)
+    ws = torch.empty(mx.workspace_size(w.T, w.d, I, w.N, w.K, w.K_s, 1 if w.dtype == "bf16" else 0),
+                     dtype=torch.uint8, device=t["u"].device)
+    h = torch.empty_like(t["u"])
+    args = (t["u"], t["E"], t["Wr"], t["Ws"], w.N, w.K, w.K_s, t["bias"])
+    for _ in range(warmup):
+        mx.layer_forward(*args, out=h, workspace=ws)
+    torch.cuda.synchronize()
+    mx.timing_read()                       # drop anything recorded before
+    mx.timing_enable(stage_timing)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        mx.layer_forward(*args, out=h, workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    mx.timing_enable(False)
+    stages = mx.timing_read()
+    return start.elapsed_time(stop), stages
+
+
+def experts_hit(mx, t, w):
+    """Distinct routed experts selected in the batch (the decode weights actually streamed)."""
+    idx, _, _ = mx.route(t["u"], t["E"], w.K, t["bias"])
+    return int(idx.unique().numel())
+
+
+def cpu_baseline(inp, n_tokens):
+    """The float64 oracle, as it stands, on the first n_tokens tokens of the workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    w = inp.w
+    routed_raw = inp.routed_all_raw(threads=16)
+    shared_raw = inp.shared_all_raw()
+    f32 = (lambda r: (r.astype(np.uint32) << 16).view(np.float32)) if w.dtype == "bf16" else (lambda r: r)
+    routed = lambda e: inp.split_block(f32(routed_raw[e]))   # noqa: E731
+    shared = lambda j: inp.split_block(f32(shared_raw[j]))   # noqa: E731
+    tokens = np.arange(min(n_tokens, w.T))
+    t0 = time.perf_counter()
+    oracle.moe_forward_tokens(inp.u_f32(), inp.E_gate_f32(), routed, shared, w.N, w.K, w.K_s,
+                              inp.gate_bias(), tokens)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {len(tokens)} of {w.T} tokens of {w.name} (router over the sample, "
+                      f"all experts' weights decoded), {dt:.2f} s wall"}
+
+
+def traffic_record(kernel_src: str, key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(key)
+    if not rec:
+        return None
+    src = open(kernel_src, "rb").read()
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_inputs
+    import mixture_experts_ffn_fp32_amd as mx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mx.load_library()
+
+    # ---- main workload
+    inp = moe_inputs.make(args.workload)
+    w = inp.w
+    t = upload(inp, dev)
+    ms, stages = time_layer(mx, t, w, args.steps, args.warmup, True)
+    ms_step = ms / args.steps
+    value = w.T * args.steps / (ms / 1e3)
+    flops_step = w.flops_per_token() * w.T
+    g1_ms, g1_n = stages["expert_gemm1_swiglu"]
+    g2_ms, g2_n = stages["expert_gemm2_down"]
+    g1_flops = 4.0 * w.d * w.I * w.T * (w.K + w.K_s)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    g1_tflops = g1_flops / (g1_ms / g1_n / 1e3) / 1e12
+    gemm1_src = os.path.join(ROOT, "mixture_experts_ffn_fp32_amd", "csrc", "expert_gemm.hip")
+    roofline = {"bound": "mfma", "kernel": "expert_gemm1_swiglu", "achieved": round(g1_tflops, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(g1_tflops / peak, 4),
+                "traffic": traffic_record(gemm1_src, f"{w.name}:expert_gemm1_swiglu"),
+                "launch_ms": round(g1_ms / g1_n, 4),
+                "algorithmic_flops_per_launch": g1_flops}
+    stage_ms = {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items()}
+    layer_tflops = flops_step / (ms_step / 1e3) / 1e12
+    del t
+    torch.cuda.empty_cache()
+
+    # ---- decode-shaped batch (HBM bound): weights of every hit expert streamed once
+    decode = None
+    if args.decode_workload:
+        dinp = moe_inputs.make(args.decode_workload)
+        dw = dinp.w
+        dt_ = upload(dinp, dev)
+        dms, dstages = time_layer(mx, dt_, dw, args.decode_steps, 10, False)
+        hit = experts_hit(mx, dt_, dw)
+        es = 2 if dw.dtype == "bf16" else 4
+        dbytes = ((hit + dw.K_s) * 3 * dw.d * dw.I * es + dw.N * dw.d * es
+                  + 2 * dw.T * dw.d * es + dw.T * dw.K * 8)
+        dstep = dms / args.decode_steps / 1e3
+        decode = {"workload": dw.name, "tokens_per_s": round(dw.T / dstep, 1),
+                  "ms_per_step": round(dstep * 1e3, 4), "experts_hit": hit,
+                  "algorithmic_bytes": dbytes, "hbm_GBs": round(dbytes / dstep / 1e9, 1),
+                  "hbm_frac": round(dbytes / dstep / 1e9 / PEAK_HBM_GBS, 4)}
+        del dt_
+        torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_sample_tokens)
+
+    line = {
+        "metric": "MoE-layer tokens/s (16B shape, bf16) + % bf16 MFMA peak / % HBM peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "routed_experts": w.N, "top_k": w.K,
+                   "shared_experts": w.K_s, "intermediate": w.I, "accumulate": "f32",
+                   "global_batch": w.T, "parallelism": "single GPU"},
+        "layer_tflops": round(layer_tflops, 2),
+        "layer_mfma_frac": round(layer_tflops / peak, 4),
+        "stage_ms": stage_ms,
+        "roofline": roofline,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

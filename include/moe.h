@@ -1,0 +1,149 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward.
+ *
+ * The operation (DeepSeekMoE paper summary, papercache.org, sec. 3.2 "Shared
+ * Expert Isolation", full layer equation; the conventional top-K layer of
+ * sec. A3 is the case K_s = 0):
+ *
+ *   s_{i,t} = Softmax_i(u_t . e_i + b_i)       over the N routed experts
+ *   g_{i,t} = s_{i,t} for the K largest s_{.,t} of token t (ties: lower i), else 0
+ *   h_t     = u_t + sum_{j<K_s} FFN_shared_j(u_t) + sum_{i<N} g_{i,t} FFN_routed_i(u_t)
+ *   FFN(x)  = W_down (SiLU(W_gate x) * (W_up x)),   SiLU(a) = a / (1 + e^-a)
+ *
+ * In the paper's notation N = mN - K_s routed experts, K = mK - K_s kept per
+ * token, and each expert's intermediate size I is the 1/m slice of sec. 3.1.
+ * The gates are not renormalised.  b is an optional per-expert logit bias.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers unless stated; the caller owns
+ *    every buffer.  The library keeps no pointer after a call returns and
+ *    never allocates or frees device memory on these paths.
+ *  - Row-major layouts.  dtype selects the storage type of u, E_gate, the
+ *    weights, h and the intermediate H / Y buffers: MOE_DTYPE_F32 (float) or
+ *    MOE_DTYPE_BF16 (bfloat16).  Router logits, softmax, gates and every
+ *    accumulation are float32 in both cases.
+ *  - One expert's weight block (W_routed holds N of them back to back,
+ *    W_shared K_s of them): W_gate [I][d], then W_up [I][d], then
+ *    W_down [d][I], contiguous, 3*I*d elements.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously; MOE_OK means "enqueued".  A fault inside a
+ *    kernel surfaces at the caller's next synchronisation.  No entry point
+ *    synchronises with the host.
+ *  - Validation runs before any HIP call.  On error nothing is enqueued, the
+ *    status says why and moe_last_error() gives a message.
+ *  - Limits: T >= 0; 1 <= K <= N <= 256; 0 <= K_s <= 16; d and I positive
+ *    multiples of 64; device pointers 16-byte aligned; inputs finite.
+ *    T = 0 is a valid empty call that enqueues nothing.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* a size, a count or a pointer is wrong          */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid input outside the implemented limits     */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required     */
+  MOE_ERR_ALIGNMENT = 4,    /* a pointer is not 16-byte aligned               */
+  MOE_ERR_HIP = 5           /* a HIP launch call failed                       */
+} moe_status_t;
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next call into the library from the same thread. */
+const char* moe_last_error(void);
+
+/* Bytes of device workspace moe_layer_forward needs for these shapes.
+ * Writes the size to *bytes (host pointer). */
+moe_status_t moe_workspace_size(int T, int d, int I, int N, int K, int K_s, int dtype,
+                                size_t* bytes);
+
+/* The whole layer forward, h = MoE(u) as above (sec. 3.2 layer equation).
+ *   u         [T][d]            dtype
+ *   E_gate    [N][d]            dtype   gate vector (centroid) e_i per routed expert
+ *   W_routed  N weight blocks   dtype
+ *   W_shared  K_s weight blocks dtype   may be NULL iff K_s == 0
+ *   gate_bias [N] float or NULL         added to the logits before the softmax
+ *   h         [T][d]            dtype   output; must not overlap any input
+ *   workspace device buffer of at least moe_workspace_size() bytes
+ * Routing ties are broken towards the lower expert index; each token's K
+ * routed contributions are summed in descending-score order, after the
+ * shared experts' sum, in float32, and h is rounded once. */
+moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_routed,
+                               const void* W_shared, int N, int K, int K_s, int T, int d,
+                               int I, int dtype, const float* gate_bias, void* h,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- stage entry points: the kernels moe_layer_forward launches, one stage
+ * at a time, for callers that want the intermediate results. ---- */
+
+/* Router (sec. A3 / 3.2 affinity and gate equations): logits z = u E_gate^T
+ * (+ gate_bias) in float32, softmax over the N routed experts, top-K.
+ *   idx    [T][K] int32   expert ids, descending score, ties lower id first
+ *   gate   [T][K] float   the kept softmax values (not renormalised)
+ *   scores [T][N] float   all softmax values, or NULL */
+moe_status_t moe_route(const void* u, const void* E_gate, const float* gate_bias, int T, int d,
+                       int N, int K, int dtype, int32_t* idx, float* gate, float* scores,
+                       void* stream);
+
+/* Workspace bytes moe_dispatch needs (per-tile counters). */
+moe_status_t moe_dispatch_workspace_size(int T, int N, int K, size_t* bytes);
+
+/* Group the (token, k) pairs by expert (the tokens each expert computes,
+ * sec. A3: token t is computed only by its K experts).  Pair p = t*K + k.
+ *   idx         [T][K] int32 input, each row holding K distinct ids in [0, N)
+ *   counts      [N]    int32 pairs per expert
+ *   offsets     [N+1]  int32 exclusive prefix sum of counts
+ *   sorted_pair [T*K]  int32 pair ids grouped by expert, ascending pair id
+ *                            (hence ascending token) within each expert */
+moe_status_t moe_dispatch(const int32_t* idx, int T, int N, int K, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_pair, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_expert_ffn needs (tile tables). */
+moe_status_t moe_expert_ffn_workspace_size(int T, int N, int K, int K_s, size_t* bytes);
+
+/* The expert FFNs on grouped tokens (SwiGLU; gate applied in the output).
+ * Inputs: offsets, sorted_pair from moe_dispatch; gate [T][K] from moe_route.
+ *   H_routed [T*K][I]     dtype  SiLU(W_gate x)*(W_up x), row = slot in sorted order
+ *   H_shared [T][K_s*I]   dtype  the same for the shared experts (expert j at
+ *                                columns j*I ..), NULL iff K_s == 0
+ *   Y        [T*K][d]     dtype  row p = t*K+k: g_{t,k} * FFN_{idx[t][k]}(u_t)
+ *   Y_shared [T][d]       dtype  sum over shared experts of FFN_j(u_t), NULL iff K_s == 0 */
+moe_status_t moe_expert_ffn(const void* u, const void* W_routed, const void* W_shared, int T,
+                            int d, int I, int N, int K, int K_s, int dtype,
+                            const int32_t* offsets, const int32_t* sorted_pair,
+                            const float* gate, void* H_routed, void* H_shared, void* Y,
+                            void* Y_shared, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Combine with the residual (sec. 3.2 layer equation):
+ *   h_t = u_t + Y_shared_t + sum_{k<K} Y_{t*K+k}, float32 sum in that order,
+ *   rounded once to dtype.  Y_shared may be NULL iff K_s == 0. */
+moe_status_t moe_combine(const void* u, const void* Y, const void* Y_shared, int T, int d,
+                         int K, int K_s, int dtype, void* h, void* stream);
+
+/* ---- per-stage timing (for profiling; off by default) ----
+ * When enabled, moe_layer_forward records a HIP event pair around each of its
+ * kernel stages on the stream it was given.  moe_timing_read() waits for
+ * those events, writes the summed milliseconds and launch counts per stage
+ * (host arrays of MOE_NUM_STAGES entries), and clears them. */
+#define MOE_NUM_STAGES 7
+/* stage order: 0 router, 1 tile ranks, 2 dispatch scan, 3 scatter,
+ *              4 expert GEMM1 (gate/up + SwiGLU), 5 expert GEMM2 (down x gate),
+ *              6 combine.  The tile-table kernel is counted in stage 4. */
+moe_status_t moe_timing_enable(int on);
+moe_status_t moe_timing_read(double* ms_per_stage, int* launches_per_stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,7 @@
+"""MI355X-native DeepSeekMoE layer forward: gfx950 HIP kernels behind a C ABI.
+
+The library (libmoe.so, built by ``python -m mixture_experts_ffn_fp32_amd.build``)
+does all of the layer's work; this package only marshals arguments to it.
+"""
+from .moe import (MoEError, STAGE_NAMES, combine, dispatch, expert_ffn, layer_forward,  # noqa: F401
+                  load_library, route, timing_enable, timing_read, workspace_size)

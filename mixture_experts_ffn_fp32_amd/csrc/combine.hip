@@ -1,0 +1,76 @@
+// Combine kernel for gfx950: h_t = u_t + Y_shared_t + sum_k Y_{t*K+k}.
+//
+// The layer output adds the shared experts' outputs, the gate-weighted
+// routed outputs and the residual (DeepSeekMoE paper summary, papercache.org,
+// sec. 3.2 layer equation).  The gates were applied when Y was written, so
+// this is a deterministic gather: each thread owns one 16-byte chunk of a
+// row of h, reads the matching chunks of u, Y_shared and the token's K rows
+// of Y (contiguous, token-major), sums in float32 in that fixed order and
+// rounds once.  HBM-bound: (K + 2) reads and one write per output element.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <class E>
+__global__ __launch_bounds__(256) void combine_kernel(const typename E::T* __restrict__ u,
+                                                      const typename E::T* __restrict__ Y,
+                                                      const typename E::T* __restrict__ Ys,
+                                                      int T, int d, int K,
+                                                      typename E::T* __restrict__ h) {
+  using Tp = typename E::T;
+  constexpr int V = E::kPerChunk;
+  const long long chunk = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = d / V;  // chunks per row
+  if (chunk >= (long long)T * cpr) return;
+  const int t = (int)(chunk / cpr);
+  const int col = (int)(chunk % cpr) * V;
+
+  float acc[V];
+  {
+    const u32x4 x = *(const u32x4*)(u + (size_t)t * d + col);
+    const Tp* xs = (const Tp*)&x;
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[j] = load_as_f32<E>(xs + j);
+  }
+  if (Ys != nullptr) {
+    const u32x4 x = *(const u32x4*)(Ys + (size_t)t * d + col);
+    const Tp* xs = (const Tp*)&x;
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[j] += load_as_f32<E>(xs + j);
+  }
+  for (int k = 0; k < K; ++k) {
+    const u32x4 x = *(const u32x4*)(Y + ((size_t)t * K + k) * d + col);
+    const Tp* xs = (const Tp*)&x;
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[j] += load_as_f32<E>(xs + j);
+  }
+  u32x4 out;
+  Tp* os = (Tp*)&out;
+#pragma unroll
+  for (int j = 0; j < V; ++j) store_from_f32<E>(os + j, acc[j]);
+  *(u32x4*)(h + (size_t)t * d + col) = out;
+}
+
+template <class E>
+hipError_t launch_t(const void* u, const void* Y, const void* Ys, int T, int d, int K, void* h,
+                    hipStream_t st) {
+  using Tp = typename E::T;
+  const long long chunks = (long long)T * (d / E::kPerChunk);
+  const long long blocks = (chunks + 255) / 256;
+  if (blocks <= 0) return hipSuccess;
+  combine_kernel<E><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+      (const Tp*)u, (const Tp*)Y, (const Tp*)Ys, T, d, K, (Tp*)h);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const void* u, const void* Y, const void* Y_shared, int T,
+                          int d, int K, int K_s, void* h, hipStream_t stream) {
+  const void* ys = K_s > 0 ? Y_shared : nullptr;
+  return dtype == 1 ? launch_t<ElemBF16>(u, Y, ys, T, d, K, h, stream)
+                    : launch_t<ElemF32>(u, Y, ys, T, d, K, h, stream);
+}
+
+}  // namespace moe

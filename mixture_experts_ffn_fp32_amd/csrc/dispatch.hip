@@ -1,0 +1,156 @@
+// Dispatch kernels for gfx950: group the (token, k) pairs by expert, stably.
+//
+// Each token is computed only by the K experts it selected (DeepSeekMoE
+// paper summary, papercache.org, sec. A3: gate sparsity).  The expert GEMMs
+// want each expert's tokens contiguous, so the pairs p = t*K + k are sorted
+// by expert, ascending p within an expert (a stable counting sort):
+//
+//  1. tile_rank: per 64-token tile, a 64-bit lane mask per expert in LDS
+//     gives each pair its rank among the tile's pairs of the same expert
+//     (popcount of the lower lanes) and each expert's count in the tile.
+//     Integer only, no global atomics, deterministic.
+//  2. dispatch_scan: one block turns tile counts into per-expert totals,
+//     offsets (exclusive scan over experts) and per-(tile, expert) bases.
+//  3. scatter: sorted_pair[base + rank] = p.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// One wavefront per tile of 64 tokens; lane = token.
+__global__ __launch_bounds__(64) void tile_rank_kernel(const int32_t* __restrict__ idx, int T,
+                                                       int N, int K,
+                                                       int32_t* __restrict__ tile_counts,
+                                                       int32_t* __restrict__ rank) {
+  __shared__ unsigned long long mask[256];
+  const int lane = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int t = tile * kRankTile + lane;
+  for (int e = lane; e < N; e += 64) mask[e] = 0ull;
+  __syncthreads();
+  const unsigned long long bit = 1ull << lane;
+  // ids outside [0, N) are ignored (the router never produces them)
+  if (t < T)
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[(size_t)t * K + k];
+      if ((unsigned)e < (unsigned)N) atomicOr(&mask[e], bit);
+    }
+  __syncthreads();
+  if (t < T) {
+    const unsigned long long below = bit - 1ull;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[(size_t)t * K + k];
+      rank[(size_t)t * K + k] = ((unsigned)e < (unsigned)N) ? __popcll(mask[e] & below) : 0;
+    }
+  }
+  for (int e = lane; e < N; e += 64) tile_counts[(size_t)tile * N + e] = __popcll(mask[e]);
+}
+
+// One block of 1024 threads.  Thread (e, g) owns expert e and the contiguous
+// chunk g of the tiles; G = 1024 / NP2 chunks per expert (NP2 = N rounded up
+// to a power of two).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ tile_counts,
+                                                             int ntiles, int N, int NP2,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tile_base) {
+  __shared__ int csum[1024];     // [g][e] chunk sums, later chunk bases
+  __shared__ int s_off[257];
+  const int tid = threadIdx.x;
+  const int e = tid % NP2, g = tid / NP2;
+  const int G = 1024 / NP2;
+  const int C = (ntiles + G - 1) / G;
+  const int lo = min(g * C, ntiles), hi = min(lo + C, ntiles);
+
+  int s = 0;
+  if (e < N)
+    for (int tl = lo; tl < hi; ++tl) s += tile_counts[(size_t)tl * N + e];
+  csum[tid] = s;
+  __syncthreads();
+  // per-expert exclusive scan over the G chunks, and the expert totals
+  if (tid < NP2) {
+    int run = 0;
+    for (int gg = 0; gg < G; ++gg) {
+      const int v = csum[gg * NP2 + tid];
+      csum[gg * NP2 + tid] = run;
+      run += v;
+    }
+    if (tid < N) {
+      counts[tid] = run;
+      s_off[tid] = run;
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the totals over experts (first wavefront, 64 at a time)
+  if (tid < 64) {
+    int carry = 0;
+    for (int b = 0; b < N; b += 64) {
+      const int v = (b + tid < N) ? s_off[b + tid] : 0;
+      const int inc = wave_inclusive_scan(v);
+      const int total = __shfl(inc, 63);
+      if (b + tid < N) s_off[b + tid] = carry + inc - v;
+      carry += total;
+    }
+    if (tid == 0) s_off[N] = carry;
+  }
+  __syncthreads();
+  for (int i = tid; i <= N; i += 1024) offsets[i] = s_off[i];
+  if (e < N) {
+    int run = s_off[e] + csum[tid];
+    for (int tl = lo; tl < hi; ++tl) {
+      tile_base[(size_t)tl * N + e] = run;
+      run += tile_counts[(size_t)tl * N + e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ rank,
+                                                      const int32_t* __restrict__ tile_base,
+                                                      int T, int N, int K,
+                                                      int32_t* __restrict__ sorted_pair) {
+  const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= (long long)T * K) return;
+  const int t = (int)(p / K);
+  const int e = idx[p];
+  if ((unsigned)e >= (unsigned)N) return;
+  sorted_pair[tile_base[(size_t)(t / kRankTile) * N + e] + rank[p]] = (int32_t)p;
+}
+
+}  // namespace
+
+hipError_t launch_tile_rank(const int32_t* idx, int T, int N, int K, int32_t* tile_counts,
+                            int32_t* rank, hipStream_t stream) {
+  const int ntiles = (T + kRankTile - 1) / kRankTile;
+  tile_rank_kernel<<<ntiles, 64, 0, stream>>>(idx, T, N, K, tile_counts, rank);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, int32_t* counts,
+                                int32_t* offsets, int32_t* tile_base, hipStream_t stream) {
+  int np2 = 1;
+  while (np2 < N) np2 <<= 1;
+  dispatch_scan_kernel<<<1, 1024, 0, stream>>>(tile_counts, ntiles, N, np2, counts, offsets,
+                                               tile_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_base,
+                          int T, int N, int K, int32_t* sorted_pair, hipStream_t stream) {
+  const long long pairs = (long long)T * K;
+  const int blocks = (int)((pairs + 255) / 256);
+  scatter_kernel<<<blocks, 256, 0, stream>>>(idx, rank, tile_base, T, N, K, sorted_pair);
+  return hipGetLastError();
+}
+
+}  // namespace moe

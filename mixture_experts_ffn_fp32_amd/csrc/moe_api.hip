@@ -1,0 +1,446 @@
+// C ABI of the DeepSeekMoE layer forward: argument validation, workspace
+// layout and the stream-ordered launch sequence.  No device memory is
+// allocated here and nothing waits on the device (except moe_timing_read).
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status_t fail(moe_status_t s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+moe_status_t ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t elem_size(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- validation
+moe_status_t check_dtype(int dtype) {
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "dtype must be MOE_DTYPE_F32 (0) or MOE_DTYPE_BF16 (1)");
+  return MOE_OK;
+}
+
+moe_status_t check_routing(int T, int N, int K) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+  if (N < 1) return fail(MOE_ERR_INVALID_ARG, "N must be >= 1");
+  if (N > 256) return fail(MOE_ERR_UNSUPPORTED, "N > 256 routed experts is not supported");
+  if (K < 1 || K > N) return fail(MOE_ERR_INVALID_ARG, "K must satisfy 1 <= K <= N");
+  if ((long long)T * K > 0x7fffffffLL - 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "T*K must stay below 2^31");
+  return MOE_OK;
+}
+
+moe_status_t check_dim(const char* name, int x) {
+  if (x <= 0) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " must be positive");
+  if (x % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, std::string(name) + " must be a multiple of 64");
+  return MOE_OK;
+}
+
+moe_status_t check_shapes(int T, int d, int I, int N, int K, int K_s, int dtype) {
+  moe_status_t s;
+  if ((s = check_dtype(dtype)) != MOE_OK) return s;
+  if ((s = check_routing(T, N, K)) != MOE_OK) return s;
+  if (K_s < 0) return fail(MOE_ERR_INVALID_ARG, "K_s must be >= 0");
+  if (K_s > 16) return fail(MOE_ERR_UNSUPPORTED, "K_s > 16 shared experts is not supported");
+  if ((s = check_dim("d", d)) != MOE_OK) return s;
+  if ((s = check_dim("I", I)) != MOE_OK) return s;
+  return MOE_OK;
+}
+
+moe_status_t check_ptr(const char* name, const void* p, bool required) {
+  if (p == nullptr) {
+    if (required) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");
+    return MOE_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(MOE_ERR_ALIGNMENT, std::string(name) + " is not 16-byte aligned");
+  return MOE_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- workspace
+struct Layout {
+  size_t idx, gate, rank, tile_counts, tile_base, counts, offsets, sorted_pair, tiles;
+  size_t H_routed, H_shared, Y, Y_shared, total;
+};
+
+int rank_tiles(int T) { return (T + moe::kRankTile - 1) / moe::kRankTile; }
+
+Layout make_layout(int T, int d, int I, int N, int K, int K_s, int dtype) {
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  const size_t TK = (size_t)T * K, es = elem_size(dtype);
+  const size_t nt = (size_t)rank_tiles(T);
+  L.idx = take(TK * 4);
+  L.gate = take(TK * 4);
+  L.rank = take(TK * 4);
+  L.tile_counts = take(nt * N * 4);
+  L.tile_base = take(nt * N * 4);
+  L.counts = take((size_t)N * 4);
+  L.offsets = take((size_t)(N + 1) * 4);
+  L.sorted_pair = take(TK * 4);
+  L.tiles = take((size_t)moe::expert_tile_table_ints(N, K_s) * 4);
+  L.H_routed = take(TK * I * es);
+  L.H_shared = take((size_t)T * K_s * I * es);
+  L.Y = take(TK * d * es);
+  L.Y_shared = take(K_s > 0 ? (size_t)T * d * es : 0);
+  L.total = o;
+  return L;
+}
+
+size_t dispatch_ws_bytes(int T, int N, int K) {
+  const size_t nt = (size_t)rank_tiles(T);
+  return align256((size_t)T * K * 4) + 2 * align256(nt * N * 4);
+}
+size_t expert_ws_bytes(int N, int K_s) {
+  return align256((size_t)moe::expert_tile_table_ints(N, K_s) * 4);
+}
+
+// ---------------------------------------------------------------- timing
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  struct Rec {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Timing g_timing;
+
+// Records an event pair around one stage when timing is on.
+struct StageScope {
+  int stage;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  StageScope(int s, hipStream_t stream) : stage(s), st(stream) {
+    std::lock_guard<std::mutex> g(g_timing.mu);
+    if (!g_timing.on) return;
+    a = g_timing.get();
+    b = g_timing.get();
+    if (a && b) (void)hipEventRecord(a, st);
+  }
+  ~StageScope() {
+    if (!(a && b)) return;
+    (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> g(g_timing.mu);
+    g_timing.recs.push_back({stage, a, b});
+  }
+};
+
+// ---------------------------------------------------------------- launches
+moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_pair, int32_t* rank,
+                          int32_t* tile_counts, int32_t* tile_base, hipStream_t st) {
+  hipError_t e;
+  {
+    StageScope sc(1, st);
+    if ((e = moe::launch_tile_rank(idx, T, N, K, tile_counts, rank, st)) != hipSuccess)
+      return hip_fail(e, "tile rank launch");
+  }
+  {
+    StageScope sc(2, st);
+    if ((e = moe::launch_dispatch_scan(tile_counts, rank_tiles(T), N, counts, offsets, tile_base,
+                                       st)) != hipSuccess)
+      return hip_fail(e, "dispatch scan launch");
+  }
+  {
+    StageScope sc(3, st);
+    if ((e = moe::launch_scatter(idx, rank, tile_base, T, N, K, sorted_pair, st)) != hipSuccess)
+      return hip_fail(e, "scatter launch");
+  }
+  return MOE_OK;
+}
+
+moe_status_t run_experts(int dtype, const moe::ExpertArgs& a, hipStream_t st) {
+  hipError_t e;
+  {
+    StageScope sc(4, st);
+    if ((e = moe::launch_tile_table(dtype, a, st)) != hipSuccess)
+      return hip_fail(e, "tile table launch");
+    if ((e = moe::launch_gemm1(dtype, a, st)) != hipSuccess)
+      return hip_fail(e, "expert GEMM1 launch");
+  }
+  {
+    StageScope sc(5, st);
+    if ((e = moe::launch_gemm2(dtype, a, st)) != hipSuccess)
+      return hip_fail(e, "expert GEMM2 launch");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status_t moe_workspace_size(int T, int d, int I, int N, int K, int K_s, int dtype,
+                                size_t* bytes) {
+  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  if (s != MOE_OK) return s;
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = T == 0 ? 0 : make_layout(T, d, I, N, K, K_s, dtype).total;
+  return ok();
+}
+
+moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_routed,
+                               const void* W_shared, int N, int K, int K_s, int T, int d, int I,
+                               int dtype, const float* gate_bias, void* h, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  if ((s = check_ptr("u", u, true)) != MOE_OK) return s;
+  if ((s = check_ptr("E_gate", E_gate, true)) != MOE_OK) return s;
+  if ((s = check_ptr("W_routed", W_routed, true)) != MOE_OK) return s;
+  if ((s = check_ptr("W_shared", W_shared, K_s > 0)) != MOE_OK) return s;
+  if ((s = check_ptr("gate_bias", gate_bias, false)) != MOE_OK) return s;
+  if ((s = check_ptr("h", h, true)) != MOE_OK) return s;
+  if ((s = check_ptr("workspace", workspace, true)) != MOE_OK) return s;
+  const size_t es = elem_size(dtype), act = (size_t)T * d * es;
+  if (overlap(h, act, u, act)) return fail(MOE_ERR_INVALID_ARG, "h overlaps u");
+  const Layout L = make_layout(T, d, I, N, K, K_s, dtype);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size()");
+  if (overlap(h, act, workspace, L.total)) return fail(MOE_ERR_INVALID_ARG, "h overlaps workspace");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* idx = (int32_t*)(ws + L.idx);
+  float* gate = (float*)(ws + L.gate);
+  hipError_t e;
+  {
+    StageScope sc(0, st);
+    if ((e = moe::launch_router(dtype, u, E_gate, gate_bias, T, d, N, K, idx, gate, nullptr, st)) !=
+        hipSuccess)
+      return hip_fail(e, "router launch");
+  }
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* sorted_pair = (int32_t*)(ws + L.sorted_pair);
+  if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
+                        (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
+                        (int32_t*)(ws + L.tile_base), st)) != MOE_OK)
+    return s;
+  moe::ExpertArgs a{};
+  a.u = u;
+  a.W_routed = W_routed;
+  a.W_shared = W_shared;
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.gate = gate;
+  a.H_routed = ws + L.H_routed;
+  a.H_shared = ws + L.H_shared;
+  a.Y = ws + L.Y;
+  a.Y_shared = ws + L.Y_shared;
+  a.tiles1 = (int32_t*)(ws + L.tiles);
+  a.tiles2 = a.tiles1 + (N + K_s + 1);
+  a.T = T;
+  a.d = d;
+  a.I = I;
+  a.N = N;
+  a.K = K;
+  a.K_s = K_s;
+  if ((s = run_experts(dtype, a, st)) != MOE_OK) return s;
+  {
+    StageScope sc(6, st);
+    if ((e = moe::launch_combine(dtype, u, a.Y, a.Y_shared, T, d, K, K_s, h, st)) != hipSuccess)
+      return hip_fail(e, "combine launch");
+  }
+  return ok();
+}
+
+moe_status_t moe_route(const void* u, const void* E_gate, const float* gate_bias, int T, int d,
+                       int N, int K, int dtype, int32_t* idx, float* gate, float* scores,
+                       void* stream) {
+  moe_status_t s;
+  if ((s = check_dtype(dtype)) != MOE_OK) return s;
+  if ((s = check_routing(T, N, K)) != MOE_OK) return s;
+  if ((s = check_dim("d", d)) != MOE_OK) return s;
+  if (T == 0) return ok();
+  if ((s = check_ptr("u", u, true)) != MOE_OK) return s;
+  if ((s = check_ptr("E_gate", E_gate, true)) != MOE_OK) return s;
+  if ((s = check_ptr("gate_bias", gate_bias, false)) != MOE_OK) return s;
+  if ((s = check_ptr("idx", idx, true)) != MOE_OK) return s;
+  if ((s = check_ptr("gate", gate, true)) != MOE_OK) return s;
+  if ((s = check_ptr("scores", scores, false)) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  StageScope sc(0, st);
+  hipError_t e = moe::launch_router(dtype, u, E_gate, gate_bias, T, d, N, K, idx, gate, scores, st);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  return ok();
+}
+
+moe_status_t moe_dispatch_workspace_size(int T, int N, int K, size_t* bytes) {
+  moe_status_t s = check_routing(T, N, K);
+  if (s != MOE_OK) return s;
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = T == 0 ? 0 : dispatch_ws_bytes(T, N, K);
+  return ok();
+}
+
+moe_status_t moe_dispatch(const int32_t* idx, int T, int N, int K, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_pair, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  moe_status_t s = check_routing(T, N, K);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  if ((s = check_ptr("idx", idx, true)) != MOE_OK) return s;
+  if ((s = check_ptr("counts", counts, true)) != MOE_OK) return s;
+  if ((s = check_ptr("offsets", offsets, true)) != MOE_OK) return s;
+  if ((s = check_ptr("sorted_pair", sorted_pair, true)) != MOE_OK) return s;
+  if ((s = check_ptr("workspace", workspace, true)) != MOE_OK) return s;
+  if (workspace_bytes < dispatch_ws_bytes(T, N, K))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_dispatch_workspace_size()");
+  char* ws = (char*)workspace;
+  const size_t nt = (size_t)rank_tiles(T);
+  int32_t* rank = (int32_t*)ws;
+  int32_t* tile_counts = (int32_t*)(ws + align256((size_t)T * K * 4));
+  int32_t* tile_base = (int32_t*)((char*)tile_counts + align256(nt * N * 4));
+  if ((s = run_dispatch(idx, T, N, K, counts, offsets, sorted_pair, rank, tile_counts, tile_base,
+                        (hipStream_t)stream)) != MOE_OK)
+    return s;
+  return ok();
+}
+
+moe_status_t moe_expert_ffn_workspace_size(int T, int N, int K, int K_s, size_t* bytes) {
+  moe_status_t s = check_routing(T, N, K);
+  if (s != MOE_OK) return s;
+  if (K_s < 0 || K_s > 16) return fail(MOE_ERR_INVALID_ARG, "K_s must satisfy 0 <= K_s <= 16");
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = T == 0 ? 0 : expert_ws_bytes(N, K_s);
+  return ok();
+}
+
+moe_status_t moe_expert_ffn(const void* u, const void* W_routed, const void* W_shared, int T,
+                            int d, int I, int N, int K, int K_s, int dtype,
+                            const int32_t* offsets, const int32_t* sorted_pair,
+                            const float* gate, void* H_routed, void* H_shared, void* Y,
+                            void* Y_shared, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  if ((s = check_ptr("u", u, true)) != MOE_OK) return s;
+  if ((s = check_ptr("W_routed", W_routed, true)) != MOE_OK) return s;
+  if ((s = check_ptr("W_shared", W_shared, K_s > 0)) != MOE_OK) return s;
+  if ((s = check_ptr("offsets", offsets, true)) != MOE_OK) return s;
+  if ((s = check_ptr("sorted_pair", sorted_pair, true)) != MOE_OK) return s;
+  if ((s = check_ptr("gate", gate, true)) != MOE_OK) return s;
+  if ((s = check_ptr("H_routed", H_routed, true)) != MOE_OK) return s;
+  if ((s = check_ptr("H_shared", H_shared, K_s > 0)) != MOE_OK) return s;
+  if ((s = check_ptr("Y", Y, true)) != MOE_OK) return s;
+  if ((s = check_ptr("Y_shared", Y_shared, K_s > 0)) != MOE_OK) return s;
+  if ((s = check_ptr("workspace", workspace, true)) != MOE_OK) return s;
+  if (workspace_bytes < expert_ws_bytes(N, K_s))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_expert_ffn_workspace_size()");
+  moe::ExpertArgs a{};
+  a.u = u;
+  a.W_routed = W_routed;
+  a.W_shared = W_shared;
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.gate = gate;
+  a.H_routed = H_routed;
+  a.H_shared = H_shared;
+  a.Y = Y;
+  a.Y_shared = Y_shared;
+  a.tiles1 = (int32_t*)workspace;
+  a.tiles2 = a.tiles1 + (N + K_s + 1);
+  a.T = T;
+  a.d = d;
+  a.I = I;
+  a.N = N;
+  a.K = K;
+  a.K_s = K_s;
+  if ((s = run_experts(dtype, a, (hipStream_t)stream)) != MOE_OK) return s;
+  return ok();
+}
+
+moe_status_t moe_combine(const void* u, const void* Y, const void* Y_shared, int T, int d, int K,
+                         int K_s, int dtype, void* h, void* stream) {
+  moe_status_t s;
+  if ((s = check_dtype(dtype)) != MOE_OK) return s;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+  if (K < 1) return fail(MOE_ERR_INVALID_ARG, "K must be >= 1");
+  if (K_s < 0) return fail(MOE_ERR_INVALID_ARG, "K_s must be >= 0");
+  if ((s = check_dim("d", d)) != MOE_OK) return s;
+  if (T == 0) return ok();
+  if ((s = check_ptr("u", u, true)) != MOE_OK) return s;
+  if ((s = check_ptr("Y", Y, true)) != MOE_OK) return s;
+  if ((s = check_ptr("Y_shared", Y_shared, K_s > 0)) != MOE_OK) return s;
+  if ((s = check_ptr("h", h, true)) != MOE_OK) return s;
+  StageScope sc(6, (hipStream_t)stream);
+  hipError_t e = moe::launch_combine(dtype, u, Y, Y_shared, T, d, K, K_s, h, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+moe_status_t moe_timing_enable(int on) {
+  std::lock_guard<std::mutex> g(g_timing.mu);
+  g_timing.on = on != 0;
+  return ok();
+}
+
+moe_status_t moe_timing_read(double* ms_per_stage, int* launches_per_stage) {
+  if (ms_per_stage == nullptr || launches_per_stage == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "output arrays are NULL");
+  std::lock_guard<std::mutex> g(g_timing.mu);
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+    ms_per_stage[i] = 0.0;
+    launches_per_stage[i] = 0;
+  }
+  moe_status_t st = MOE_OK;
+  for (auto& r : g_timing.recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) {
+      st = hip_fail(e, "timing event");
+    } else if (r.stage >= 0 && r.stage < MOE_NUM_STAGES) {
+      ms_per_stage[r.stage] += ms;
+      launches_per_stage[r.stage] += 1;
+    }
+    g_timing.pool.push_back(r.a);
+    g_timing.pool.push_back(r.b);
+  }
+  g_timing.recs.clear();
+  return st == MOE_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- types
+using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+using f32x4 = float __attribute__((ext_vector_type(4)));
+using f32x16 = float __attribute__((ext_vector_type(16)));
+using bf16x8 = __bf16 __attribute__((ext_vector_type(8)));
+
+// Element traits: storage type and how many elements one 16-byte chunk holds.
+struct ElemF32 {
+  using T = float;
+  static constexpr int kPerChunk = 4;
+};
+struct ElemBF16 {
+  using T = uint16_t;  // bfloat16 bit pattern
+  static constexpr int kPerChunk = 8;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(uint32_t(b) << 16);
+}
+// float -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t x = __float_as_uint(f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return uint16_t((x >> 16) | 0x40u);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return uint16_t(x >> 16);
+}
+
+template <class E>
+__device__ __forceinline__ float load_as_f32(const typename E::T* p);
+template <>
+__device__ __forceinline__ float load_as_f32<ElemF32>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_as_f32<ElemBF16>(const uint16_t* p) {
+  return bf16_to_f32(*p);
+}
+
+template <class E>
+__device__ __forceinline__ void store_from_f32(typename E::T* p, float v);
+template <>
+__device__ __forceinline__ void store_from_f32<ElemF32>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_from_f32<ElemBF16>(uint16_t* p, float v) {
+  *p = f32_to_bf16(v);
+}
+
+// ---------------------------------------------------------------- LDS tiles
+// A tile row holds 128 bytes of the contraction dimension as 8 chunks of 16
+// bytes.  Chunk c of row r lives at chunk slot c ^ ((r >> 1) & 7): 16 lanes
+// reading 16 consecutive rows at one chunk index then touch 16 distinct
+// 16-byte bank groups (two rows span the 256-byte bank width).
+__device__ __forceinline__ int lds_chunk_offset(int r, int c) {
+  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// ---------------------------------------------------------------- launchers
+// Router: logits, softmax, top-K.  Returns hipError_t of the launch.
+hipError_t launch_router(int dtype, const void* u, const void* E_gate, const float* bias, int T,
+                         int d, int N, int K, int32_t* idx, float* gate, float* scores,
+                         hipStream_t stream);
+
+// Dispatch: per-64-token tile ranks, global scan, scatter.
+constexpr int kRankTile = 64;
+hipError_t launch_tile_rank(const int32_t* idx, int T, int N, int K, int32_t* tile_counts,
+                            int32_t* rank, hipStream_t stream);
+hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, int32_t* counts,
+                                int32_t* offsets, int32_t* tile_base, hipStream_t stream);
+hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_base,
+                          int T, int N, int K, int32_t* sorted_pair, hipStream_t stream);
+
+// Expert GEMMs.
+struct ExpertArgs {
+  const void* u;
+  const void* W_routed;
+  const void* W_shared;
+  const int32_t* offsets;      // [N+1]
+  const int32_t* sorted_pair;  // [T*K]
+  const float* gate;           // [T*K]
+  void* H_routed;              // [T*K][I]
+  void* H_shared;              // [T][K_s*I]
+  void* Y;                     // [T*K][d]
+  void* Y_shared;              // [T][d]
+  int32_t* tiles1;             // [N+K_s+1] m-tile prefix for GEMM1
+  int32_t* tiles2;             // [N+2]     m-tile prefix for GEMM2
+  int T, d, I, N, K, K_s;
+};
+int expert_tile_table_ints(int N, int K_s);
+hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream);
+hipError_t launch_gemm1(int dtype, const ExpertArgs& a, hipStream_t stream);
+hipError_t launch_gemm2(int dtype, const ExpertArgs& a, hipStream_t stream);
+
+hipError_t launch_combine(int dtype, const void* u, const void* Y, const void* Y_shared, int T,
+                          int d, int K, int K_s, void* h, hipStream_t stream);
+
+}  // namespace moe

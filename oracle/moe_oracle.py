@@ -45,7 +45,8 @@ __all__ = [
     "affinity_logits", "affinity_scores", "top_k_gates", "swiglu_ffn",
     "moe_layer_forward", "moe_forward_tokens", "dense_gate_weighted_forward",
     "permute_by_expert", "expert_slot_activations", "balance_statistics",
-    "brute_force_top_k",
+    "brute_force_top_k", "moe_forward_given_routing", "near_tie_alternatives",
+    "combine_outputs",
 ]
 
 
@@ -178,6 +179,44 @@ def moe_layer_forward(u, E_gate, routed, shared, N: int, K: int, K_s: int, gate_
     return moe_forward_tokens(u, E_gate, routed, shared, N, K, K_s, gate_bias, None)
 
 
+def moe_forward_given_routing(u, idx, g, routed, shared, K_s: int):
+    """h_t = u_t + sum_j FFN_shared_j(u_t) + sum_k g[t,k] FFN_{idx[t,k]}(u_t) for given gates.
+
+    The same layer equation with the routing supplied (used where a token's
+    top-K set is not unique, to evaluate each admissible set).
+    """
+    u = _f64(u)
+    idx = np.asarray(idx)
+    g = _f64(g)
+    h = u.copy()
+    for j in range(K_s):
+        h += swiglu_ffn(u, *_expert(shared, j))
+    for e in np.unique(idx):
+        rows, ks = np.nonzero(idx == e)
+        h[rows] += g[rows, ks][:, None] * swiglu_ffn(u[rows], *_expert(routed, int(e)))
+    return h
+
+
+def near_tie_alternatives(s, K: int, eps: float = 1e-6):
+    """For tokens whose K-th and (K+1)-th scores are within eps, the other admissible set.
+
+    Returns {t: (idx_alt [K], g_alt [K])}: the top-K set with its K-th expert
+    replaced by the (K+1)-th.  Either set satisfies "keep the K largest" up to
+    eps, so either is a correct routing in finite precision.
+    """
+    s = _f64(s)
+    idx, g, margin = top_k_gates(s, K)
+    out = {}
+    if K >= s.shape[1]:
+        return out
+    order = np.argsort(-s, axis=1, kind="stable")
+    for t in np.nonzero(margin <= eps)[0]:
+        alt = idx[t].copy()
+        alt[K - 1] = order[t, K]
+        out[int(t)] = (alt, s[t, alt])
+    return out
+
+
 def dense_gate_weighted_forward(u, E_gate, routed, gate_bias=None):
     """h_t = u_t + sum_i s_{i,t} FFN_i(u_t) over all N experts, no selection at all.
 
@@ -244,6 +283,18 @@ def expert_slot_activations(u, routed, shared, idx, g, sorted_pair, offsets, K: 
             H = a / (1.0 + np.exp(-a)) * b
         sh[j] = (H, H @ Wd.T)
     return out, sh
+
+
+def combine_outputs(u, Y, Y_shared, K: int):
+    """h_t = u_t + Y_shared_t + sum_k Y[t*K + k]: the layer equation's final sum, float64.
+
+    Y [T*K][d] holds gate-weighted routed outputs in token-major pair order,
+    Y_shared [T][d] (or None) the summed shared-expert outputs.
+    """
+    u = _f64(u)
+    T, d = u.shape
+    h = u + (0.0 if Y_shared is None else _f64(Y_shared))
+    return h + _f64(Y).reshape(T, K, d).sum(axis=1)
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,120 @@
+"""The C ABI on the CPU: the library loads, exports what include/moe.h declares,
+and rejects bad arguments before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+mx = pytest.importorskip("mixture_experts_ffn_fp32_amd")
+from mixture_experts_ffn_fp32_amd import moe as binding  # noqa: E402
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, ALIGNMENT = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libmoe.so is not built: run python -m mixture_experts_ffn_fp32_amd.build")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def _ws(lib, *shape):
+    out = ctypes.c_size_t(0)
+    st = lib.moe_workspace_size(*shape, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_validation(lib):
+    # T, d, I, N, K, K_s, dtype
+    assert _ws(lib, 8192, 2048, 1408, 64, 6, 2, 1)[0] == OK
+    assert _ws(lib, 0, 2048, 1408, 64, 6, 2, 1) == (OK, 0)
+    cases = [
+        ((8192, 2048, 1400, 64, 6, 2, 1), UNSUPPORTED),   # I not a multiple of 64
+        ((8192, 2000, 1408, 64, 6, 2, 1), UNSUPPORTED),   # d not a multiple of 64
+        ((8192, 2048, 1408, 64, 65, 2, 1), INVALID),      # K > N
+        ((8192, 2048, 1408, 64, 0, 2, 1), INVALID),       # K < 1
+        ((8192, 2048, 1408, 0, 1, 2, 1), INVALID),        # N < 1
+        ((8192, 2048, 1408, 257, 6, 2, 1), UNSUPPORTED),  # N > 256
+        ((8192, 2048, 1408, 64, 6, 17, 1), UNSUPPORTED),  # K_s > 16
+        ((8192, 2048, 1408, 64, 6, -1, 1), INVALID),
+        ((-1, 2048, 1408, 64, 6, 2, 1), INVALID),
+        ((8192, 2048, 1408, 64, 6, 2, 7), UNSUPPORTED),   # dtype
+        ((8192, 0, 1408, 64, 6, 2, 1), INVALID),
+    ]
+    for shape, want in cases:
+        st, _ = _ws(lib, *shape)
+        assert st == want, (shape, st, lib.moe_last_error())
+        assert lib.moe_last_error().decode()
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    sizes = [_ws(lib, T, 2048, 1408, 64, 6, 2, 1)[1] for T in (1, 64, 65, 1000, 8192)]
+    assert sizes == sorted(sizes) and len(set(sizes)) == len(sizes)
+    # at least the token-proportional buffers: H (T*K + T*K_s) * I and Y (T*K + T) * d
+    T = 8192
+    assert sizes[-1] >= 2 * (T * 8 * 1408 + T * 7 * 2048)
+
+
+def _fwd(lib, u=16, E=16, Wr=16, Ws=16, h=1 << 20, ws=1 << 24, wsb=1 << 40, N=64, K=6, K_s=2, T=8,
+         d=2048, I=1408, dt=1, bias=None):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)   # noqa: E731
+    return lib.moe_layer_forward(p(u), p(E), p(Wr), p(Ws), N, K, K_s, T, d, I, dt, p(bias), p(h),
+                                 p(ws), wsb, None)
+
+
+def test_forward_validation_never_reaches_the_gpu(lib):
+    # every case fails validation, which runs before any HIP call
+    assert _fwd(lib, u=None) == INVALID
+    assert _fwd(lib, u=8) == ALIGNMENT
+    assert _fwd(lib, Ws=None) == INVALID
+    assert _fwd(lib, bias=4) == ALIGNMENT
+    assert _fwd(lib, ws=None) == INVALID
+    assert _fwd(lib, wsb=1024) == WORKSPACE
+    assert _fwd(lib, h=16) == INVALID                   # h overlaps u
+    assert _fwd(lib, K=0) == INVALID
+    assert _fwd(lib, I=100) == UNSUPPORTED
+    assert _fwd(lib, dt=3) == UNSUPPORTED
+    assert "aligned" in (_fwd(lib, u=8), lib.moe_last_error().decode())[1]
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _fwd(lib, T=0, u=None, h=None, ws=None, wsb=0) == OK
+
+
+def test_stage_validation(lib):
+    p = ctypes.c_void_p
+    assert lib.moe_route(None, p(16), None, 4, 64, 8, 9, 1, p(16), p(16), None, None) == INVALID
+    assert lib.moe_route(p(16), p(16), None, 4, 65, 8, 2, 1, p(16), p(16), None, None) == UNSUPPORTED
+    assert lib.moe_dispatch(p(16), 4, 8, 2, p(16), p(16), p(16), p(16), 0, None) == WORKSPACE
+    out = ctypes.c_size_t(0)
+    assert lib.moe_dispatch_workspace_size(4, 8, 2, ctypes.byref(out)) == OK and out.value > 0
+    assert lib.moe_expert_ffn_workspace_size(4, 8, 2, 1, ctypes.byref(out)) == OK and out.value > 0
+    assert lib.moe_combine(p(16), None, None, 4, 64, 2, 0, 1, p(4096), None) == INVALID
+    assert lib.moe_combine(p(16), p(32), None, 4, 64, 2, 1, 1, p(4096), None) == INVALID
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    u = torch.zeros(4, 64)
+    with pytest.raises(mx.MoEError):
+        mx.layer_forward(u, torch.zeros(8, 64), torch.zeros(8 * 3 * 64 * 64), None, 8, 2, 0)

@@ -1,0 +1,168 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Stage tests feed the GPU and the oracle the same inputs (seeded inputs, or
+the oracle's own routing / dispatch / expert outputs) and compare each stage;
+end-to-end tests compare h.  Shapes span several tiles with ragged tails,
+and include the degenerate cases (one token, K = N, no shared expert,
+N = 1, N = 256, a non-power-of-two N).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+from parity_helpers import (Uploaded, check_h, check_routing, device_f32, say, to_device,
+                            tol_for)
+
+pytestmark = pytest.mark.gpu
+
+mx = pytest.importorskip("mixture_experts_ffn_fp32_amd")
+
+SMALL = {
+    "ragged_f32": dict(T=300, d=256, N=20, K=5, K_s=2, I=192, dtype="f32"),
+    "ragged_bf16": dict(T=300, d=256, N=20, K=5, K_s=2, I=192, dtype="bf16"),
+    "no_shared_bf16": dict(T=200, d=128, N=8, K=2, K_s=0, I=128, dtype="bf16"),
+    "k_equals_n_f32": dict(T=70, d=64, N=6, K=6, K_s=1, I=64, dtype="f32"),
+    "one_token_bf16": dict(T=1, d=128, N=16, K=4, K_s=1, I=128, dtype="bf16"),
+    "n63_bf16": dict(T=513, d=320, N=63, K=7, K_s=1, I=128, dtype="bf16"),
+    "n256_bf16": dict(T=130, d=128, N=256, K=8, K_s=3, I=64, dtype="bf16"),
+    "n1_f32": dict(T=33, d=64, N=1, K=1, K_s=0, I=64, dtype="f32"),
+    "wide_tokens_bf16": dict(T=2050, d=512, N=16, K=4, K_s=1, I=256, dtype="bf16"),
+}
+
+
+def small_inputs(name):
+    kw = dict(SMALL[name])
+    return moe_inputs.custom(**kw, sigma=0.08, seed=1000 + sorted(SMALL).index(name), name=name)
+
+
+@pytest.fixture(scope="module", params=sorted(SMALL))
+def small(request):
+    say(f"upload {request.param}")
+    return Uploaded(small_inputs(request.param))
+
+
+def test_route(small):
+    w = small.w
+    say(f"route {w.name}")
+    idx, gate, scores = mx.route(small.u, small.E, w.K, small.bias, want_scores=True)
+    torch.cuda.synchronize()
+    s_ref = oracle.affinity_scores(small.inp.u_f32(), small.inp.E_gate_f32(), small.inp.gate_bias())
+    sc = scores.cpu().numpy()
+    assert np.all(np.abs(sc - s_ref) <= 1e-5 * s_ref + 1e-9)
+    check_routing(idx.cpu().numpy(), gate.cpu().numpy(), s_ref, w.K)
+
+
+def test_dispatch(small):
+    w = small.w
+    s_ref = oracle.affinity_scores(small.inp.u_f32(), small.inp.E_gate_f32(), small.inp.gate_bias())
+    idx_ref, _, _ = oracle.top_k_gates(s_ref, w.K)
+    say(f"dispatch {w.name}")
+    counts, offsets, sp = mx.dispatch(torch.from_numpy(idx_ref.astype(np.int32)).cuda(), w.N)
+    torch.cuda.synchronize()
+    c_ref, o_ref, sp_ref = oracle.permute_by_expert(idx_ref, w.N)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), o_ref)
+    np.testing.assert_array_equal(sp.cpu().numpy(), sp_ref)
+
+
+def test_expert_ffn(small):
+    w = small.w
+    inp = small.inp
+    u = inp.u_f32()
+    s_ref = oracle.affinity_scores(u, inp.E_gate_f32(), inp.gate_bias())
+    idx_ref, g_ref, _ = oracle.top_k_gates(s_ref, w.K)
+    _, o_ref, sp_ref = oracle.permute_by_expert(idx_ref, w.N)
+    say(f"expert_ffn {w.name}")
+    H, Hs, Y, Ys = mx.expert_ffn(small.u, small.W_routed, small.W_shared, w.N, w.K, w.K_s,
+                                 torch.from_numpy(o_ref.astype(np.int32)).cuda(),
+                                 torch.from_numpy(sp_ref.astype(np.int32)).cuda(),
+                                 torch.from_numpy(g_ref.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    per_e, per_s = oracle.expert_slot_activations(u, small.routed, small.shared, idx_ref, g_ref,
+                                                  sp_ref, o_ref, w.K, w.K_s)
+    tol = tol_for(w)
+    Hg, Yg = device_f32(H), device_f32(Y)
+    for e, (H_ref, Y_ref) in per_e.items():
+        lo, hi = o_ref[e], o_ref[e + 1]
+        if hi == lo:
+            continue
+        assert np.abs(Hg[lo:hi] - H_ref).max() <= tol * np.abs(H_ref).max(), f"H of expert {e}"
+        rows = sp_ref[lo:hi]
+        assert np.abs(Yg[rows] - Y_ref).max() <= tol * np.abs(Y_ref).max(), f"Y of expert {e}"
+    if w.K_s:
+        Hsg, Ysg = device_f32(Hs), device_f32(Ys)
+        Ys_ref = sum(per_s[j][1] for j in range(w.K_s))
+        for j in range(w.K_s):
+            H_ref = per_s[j][0]
+            got = Hsg[:, j * w.I:(j + 1) * w.I]
+            assert np.abs(got - H_ref).max() <= tol * np.abs(H_ref).max(), f"H of shared {j}"
+        assert np.abs(Ysg - Ys_ref).max() <= tol * np.abs(Ys_ref).max(), "Y_shared"
+
+
+def test_combine(small):
+    w = small.w
+    rng = np.random.default_rng(5)
+    T, d, K = w.T, w.d, w.K
+    # any values do for this stage; round them to the storage type first
+    Yr = (rng.standard_normal((T * K, d)) * 0.1).astype(np.float32)
+    Ysr = (rng.standard_normal((T, d)) * 0.1).astype(np.float32)
+    if w.dtype == "bf16":
+        Yr, Ysr = moe_inputs.f32_to_bf16_bits(Yr), moe_inputs.f32_to_bf16_bits(Ysr)
+        Yf, Ysf = moe_inputs.bf16_bits_to_f32(Yr), moe_inputs.bf16_bits_to_f32(Ysr)
+    else:
+        Yf, Ysf = Yr, Ysr
+    say(f"combine {w.name}")
+    h = mx.combine(small.u, to_device(Yr, w.dtype), to_device(Ysr, w.dtype) if w.K_s else None,
+                   K, w.K_s)
+    torch.cuda.synchronize()
+    ref = oracle.combine_outputs(small.inp.u_f32(), Yf, Ysf if w.K_s else None, K)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - (7 if w.dtype == "bf16" else 21))
+    assert np.all(np.abs(device_f32(h) - ref) <= ulp)
+
+
+def test_layer_forward(small):
+    w = small.w
+    say(f"layer_forward {w.name}")
+    h = mx.layer_forward(small.u, small.E, small.W_routed, small.W_shared, w.N, w.K, w.K_s,
+                         small.bias)
+    idx, gate, _ = mx.route(small.u, small.E, w.K, small.bias)
+    torch.cuda.synchronize()
+    inp = small.inp
+    h_ref, info = oracle.moe_forward_tokens(inp.u_f32(), inp.E_gate_f32(), small.routed,
+                                            small.shared, w.N, w.K, w.K_s, inp.gate_bias())
+    differing, alts = check_routing(idx.cpu().numpy(), gate.cpu().numpy(), info["s"], w.K)
+    for t in differing:   # an admissible near-tie set: compare with the oracle's h for that set
+        a_idx, a_g = alts[int(t)]
+        h_ref[t] = oracle.moe_forward_given_routing(inp.u_f32()[t:t + 1], a_idx[None], a_g[None],
+                                                    small.routed, small.shared, w.K_s)[0]
+    check_h(device_f32(h), h_ref, inp.u_f32().astype(np.float64), tol_for(w), w.dtype, w.name)
+
+
+def test_deterministic_and_chunk_invariant(small):
+    w = small.w
+    if w.T < 4:
+        pytest.skip("needs a few tokens")
+    say(f"determinism {w.name}")
+    args = (small.E, small.W_routed, small.W_shared, w.N, w.K, w.K_s, small.bias)
+    h1 = mx.layer_forward(small.u, *args)
+    h2 = mx.layer_forward(small.u, *args)
+    a = w.T // 3
+    ha = mx.layer_forward(small.u[:a].contiguous(), *args)
+    hb = mx.layer_forward(small.u[a:].contiguous(), *args)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    hc = torch.cat([ha, hb])
+    tol = tol_for(w) * h1.float().abs().max().item()
+    assert (hc.float() - h1.float()).abs().max().item() <= tol
+
+
+def test_empty_batch():
+    inp = small_inputs("ragged_bf16")
+    up = Uploaded(inp)
+    w = inp.w
+    say("empty batch")
+    h = mx.layer_forward(up.u[:0], up.E, up.W_routed, up.W_shared, w.N, w.K, w.K_s)
+    torch.cuda.synchronize()
+    assert h.shape == (0, w.d)

@@ -372,3 +372,37 @@ def test_balance_statistics_closed_forms():
     idx3 = np.tile(np.arange(K), (T2, 1))
     st3 = oracle.balance_statistics(s2, idx3, K)
     np.testing.assert_allclose(st3["f"], [N / K] * K + [0] * (N - K))
+
+
+def test_given_routing_equals_layer_and_identical_experts():
+    # with the oracle's own routing it reproduces the layer; with identical experts it
+    # gives u + shared + (sum of the supplied gates) FFN(u) for any supplied set
+    inp = moe_inputs.custom(T=12, d=32, N=6, K=2, K_s=1, I=16, seed=13)
+    u, E = inp.u_f32(), inp.E_gate_f32()
+    h, info = oracle.moe_layer_forward(u, E, inp.routed_expert_f32, inp.shared_expert_f32, 6, 2, 1)
+    h2 = oracle.moe_forward_given_routing(u, info["idx"], info["g"], inp.routed_expert_f32,
+                                          inp.shared_expert_f32, 1)
+    np.testing.assert_allclose(h2, h, atol=1e-14)
+    W = _one_unit_expert()
+    u1 = np.array([[1.0, 0.0], [1.0, 0.0]])
+    h3 = oracle.moe_forward_given_routing(u1, np.array([[0, 2], [1, 0]]), np.array([[0.25, 0.5], [0.125, 0.0]]),
+                                          [W, W, W], [], 0)
+    ffn = 0.75 * LN3 * np.array([1.0, 2.0])
+    np.testing.assert_allclose(h3, [u1[0] + 0.75 * ffn, u1[1] + 0.125 * ffn], atol=1e-14)
+
+
+def test_near_tie_alternative_swaps_boundary_expert():
+    s = np.array([[0.3, 0.2, 0.2 + 5e-7, 0.1, 0.2 - 1e-3 + 0.0]])
+    s = s / s.sum()
+    alts = oracle.near_tie_alternatives(s, 2)
+    assert list(alts) == [0]
+    assert sorted(alts[0][0].tolist()) == [0, 1]      # expert 2 (K-th) swapped for expert 1
+    assert oracle.near_tie_alternatives(s, 1) == {}
+
+
+def test_combine_outputs_closed_form():
+    u = np.array([[1.0, 2.0], [3.0, 4.0]])
+    Y = np.array([[0.5, 0.0], [0.0, 0.25], [1.0, 1.0], [2.0, -2.0]])   # T = 2, K = 2
+    Ys = np.array([[10.0, 20.0], [30.0, 40.0]])
+    np.testing.assert_array_equal(oracle.combine_outputs(u, Y, Ys, 2), [[11.5, 22.25], [36.0, 43.0]])
+    np.testing.assert_array_equal(oracle.combine_outputs(u, Y, None, 2), [[1.5, 2.25], [6.0, 3.0]])
