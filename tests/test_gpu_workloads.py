@@ -1,0 +1,147 @@
+"""GPU parity at the five workload shapes (tiny fp32, 2B-, 16B-prefill-, 16B-decode- and
+145B-skewed-shaped bf16 layers), in the launch configuration the benchmark times.
+
+Routing is checked on every token; dispatch on every pair (integer exact); the
+expert stage on the hottest, the coldest and two random experts; h on every
+token where the oracle finishes in seconds, else on a sample that holds the
+first and last tokens, every near-tie token, tokens of the hottest and coldest
+experts and random tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+from parity_helpers import (Uploaded, check_h, check_routing, device_f32, say, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+mx = pytest.importorskip("mixture_experts_ffn_fp32_amd")
+
+# tokens whose h is recomputed by the oracle (None = all)
+SAMPLE = {"tiny_fp32": None, "moe16b_decode_bf16": None, "moe2b_bf16": 384,
+          "moe16b_prefill_bf16": 192, "moe145b_skewed_bf16": 96}
+
+
+@pytest.fixture(scope="module", params=list(moe_inputs.WORKLOADS))
+def wl(request):
+    name = request.param
+    say(f"upload workload {name}")
+    up = Uploaded(moe_inputs.make(name))
+    inp = up.inp
+    s = oracle.affinity_scores(inp.u_f32(), inp.E_gate_f32(), inp.gate_bias())
+    yield up, s
+    del up
+    torch.cuda.empty_cache()
+
+
+def _sample(up, s, n):
+    w = up.w
+    if n is None or n >= w.T:
+        return np.arange(w.T)
+    idx, _, margin = oracle.top_k_gates(s, w.K)
+    counts = np.bincount(idx.ravel(), minlength=w.N)
+    hot = int(np.argmax(counts))
+    nz = np.nonzero(counts)[0]
+    cold = int(nz[np.argmin(counts[nz])])
+    rng = np.random.default_rng(w.seed)
+    pick = {0, w.T - 1}
+    pick |= set(np.nonzero(margin <= 1e-6)[0].tolist())
+    pick |= set(np.nonzero((idx == cold).any(axis=1))[0][:8].tolist())
+    pick |= set(np.nonzero((idx == hot).any(axis=1))[0][:8].tolist())
+    while len(pick) < n:
+        pick.add(int(rng.integers(w.T)))
+    return np.array(sorted(pick))
+
+
+def test_routing_all_tokens(wl):
+    up, s = wl
+    w = up.w
+    say(f"route {w.name}")
+    idx, gate, _ = mx.route(up.u, up.E, w.K, up.bias)
+    torch.cuda.synchronize()
+    differing, _ = check_routing(idx.cpu().numpy(), gate.cpu().numpy(), s, w.K)
+    assert len(differing) <= max(1, w.T // 1000)
+
+
+def test_dispatch_all_pairs(wl):
+    up, s = wl
+    w = up.w
+    idx_ref, _, _ = oracle.top_k_gates(s, w.K)
+    say(f"dispatch {w.name}")
+    counts, offsets, sp = mx.dispatch(torch.from_numpy(idx_ref.astype(np.int32)).cuda(), w.N)
+    torch.cuda.synchronize()
+    c_ref, o_ref, sp_ref = oracle.permute_by_expert(idx_ref, w.N)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), o_ref)
+    np.testing.assert_array_equal(sp.cpu().numpy(), sp_ref)
+    if w.zipf_s is not None:   # the skew really is there
+        assert c_ref.max() > 5 * c_ref.mean()
+
+
+def test_expert_stage_selected_experts(wl):
+    up, s = wl
+    w = up.w
+    idx_ref, g_ref, _ = oracle.top_k_gates(s, w.K)
+    c_ref, o_ref, sp_ref = oracle.permute_by_expert(idx_ref, w.N)
+    say(f"expert_ffn {w.name}")
+    H, Hs, Y, Ys = mx.expert_ffn(up.u, up.W_routed, up.W_shared, w.N, w.K, w.K_s,
+                                 torch.from_numpy(o_ref.astype(np.int32)).cuda(),
+                                 torch.from_numpy(sp_ref.astype(np.int32)).cuda(),
+                                 torch.from_numpy(g_ref.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    nz = np.nonzero(c_ref)[0]
+    rng = np.random.default_rng(3)
+    experts = sorted({int(np.argmax(c_ref)), int(nz[np.argmin(c_ref[nz])]),
+                      *rng.choice(nz, size=min(2, nz.size), replace=False).tolist()})
+    tol = tol_for(w)
+    # at most 256 rows per expert keep the oracle's share of the time bounded
+    for e in experts:
+        lo, hi = int(o_ref[e]), int(o_ref[e + 1])
+        hi = min(hi, lo + 256)
+        pairs = sp_ref[lo:hi]
+        # H and Y of these rows from the oracle's own slot activations
+        o_one = np.zeros(w.N + 1, dtype=np.int64)
+        o_one[e + 1:] = hi - lo
+        sp_one = np.zeros(hi - lo, dtype=np.int64)
+        sp_one[:] = pairs
+        acts, _ = oracle.expert_slot_activations(up.inp.u_f32(), up.routed, up.shared, idx_ref,
+                                                 g_ref, sp_one, o_one, w.K, 0, experts=[e])
+        H_ref, Y_ref = acts[e]
+        Hg = device_f32(H[lo:hi])
+        Yg = device_f32(Y[torch.from_numpy(pairs).cuda()])
+        assert np.abs(Hg - H_ref).max() <= tol * np.abs(H_ref).max(), f"H of expert {e}"
+        assert np.abs(Yg - Y_ref).max() <= tol * np.abs(Y_ref).max(), f"Y of expert {e}"
+    if w.K_s:
+        rows = np.arange(min(w.T, 128))
+        _, sh = oracle.expert_slot_activations(up.inp.u_f32()[rows], up.routed, up.shared,
+                                               idx_ref[rows], g_ref[rows], sp_ref[:0],
+                                               np.zeros(1, dtype=np.int64), w.K, w.K_s, experts=[])
+        Ys_ref = sum(sh[j][1] for j in range(w.K_s))
+        Ysg = device_f32(Ys[:len(rows)])
+        assert np.abs(Ysg - Ys_ref).max() <= tol * np.abs(Ys_ref).max(), "Y_shared"
+
+
+def test_layer_forward_sampled(wl):
+    up, s = wl
+    w = up.w
+    say(f"layer_forward {w.name}")
+    h = mx.layer_forward(up.u, up.E, up.W_routed, up.W_shared, w.N, w.K, w.K_s, up.bias)
+    idx, gate, _ = mx.route(up.u, up.E, w.K, up.bias)
+    torch.cuda.synchronize()
+    tokens = _sample(up, s, SAMPLE[w.name])
+    inp = up.inp
+    h_ref, info = oracle.moe_forward_tokens(inp.u_f32(), inp.E_gate_f32(), up.routed, up.shared,
+                                            w.N, w.K, w.K_s, inp.gate_bias(), tokens)
+    idx_s = idx.cpu().numpy()[tokens]
+    differing, alts = check_routing(idx_s, gate.cpu().numpy()[tokens], info["s"], w.K)
+    for i in differing:
+        a_idx, a_g = alts[int(i)]
+        t = tokens[i]
+        h_ref[i] = oracle.moe_forward_given_routing(inp.u_f32()[t:t + 1], a_idx[None], a_g[None],
+                                                    up.routed, up.shared, w.K_s)[0]
+    hs = device_f32(h[torch.from_numpy(tokens).cuda()])
+    rel = check_h(hs, h_ref, inp.u_f32()[tokens].astype(np.float64), tol_for(w), w.dtype, w.K,
+                  w.name)
+    say(f"{w.name}: max|dh|/max|h| = {rel:.2e} over {len(tokens)} tokens")
