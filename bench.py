@@ -37,7 +37,34 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--profile-mode", action="store_true",
+                    help="for hardware-counter runs: a 1 GiB device copy (calibration) and two "
+                         "layer forwards of the workload, nothing else")
     return ap.parse_args()
+
+
+def profile_mode(args):
+    """Short, fixed sequence for rocprofv3 counter passes: torch's copy kernel moving a known
+    1 GiB (reads 1 GiB, writes 1 GiB) three times, then two forwards of the workload."""
+    import torch
+
+    import moe_inputs
+    import mixture_experts_ffn_fp32_amd as mx
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    inp = moe_inputs.make(args.workload)
+    t = upload(inp, dev)
+    w = inp.w
+    for _ in range(2):
+        mx.layer_forward(t["u"], t["E"], t["Wr"], t["Ws"], w.N, w.K, w.K_s, t["bias"])
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_mode": w.name, "copy_bytes_each_way": 1 << 30}), flush=True)
 
 
 def upload(inp, device):
@@ -133,6 +160,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.profile_mode:
+        return profile_mode(args)
     import torch
 
     import moe_inputs

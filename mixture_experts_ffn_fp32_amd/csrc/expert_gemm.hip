@@ -21,6 +21,12 @@
 // the expert's weight tile, and the block id is remapped so that each XCD
 // (workgroups are dealt round-robin over the 8 XCDs) owns a contiguous range
 // of tiles and its L2 holds that expert's weights and tokens.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -83,11 +89,197 @@ __global__ __launch_bounds__(64) void tile_table_kernel(const int32_t* __restric
   }
 }
 
+// ---------------------------------------------------------------- shared pieces
+// The tile of one block: virtual expert v, its first output column n0, first
+// row m0, and the expert's slot range.
+struct Tile {
+  int v, n0, m0, row_base, rows;
+  bool routed;
+};
+
+// Maps the block to its tile through the tile table (m fastest within an
+// expert).  Returns false if the block has no tile (grids are sized for the
+// worst case, so the highest block ids may find none).  Every thread of the
+// block gets the same answer.
+template <int BM, int BNO, int MODE>
+__device__ __forceinline__ bool find_tile(const ExpertArgs& a, int* s_tab, int* s_v, Tile& ti) {
+  const int tid = threadIdx.x;
+  const int V = MODE == 1 ? a.N + a.K_s : a.N + (a.K_s > 0 ? 1 : 0);
+  const int32_t* tab = MODE == 1 ? a.tiles1 : a.tiles2;
+  const int nt = (MODE == 1 ? a.I : a.d) / BNO;
+  for (int i = tid; i <= V; i += blockDim.x) s_tab[i] = tab[i];
+  __syncthreads();
+  // blocks past the real tile count leave; the rest are dealt over the XCDs
+  const int total = s_tab[V] * nt;
+  if ((int)blockIdx.x >= total) return false;
+  const int L = xcd_swizzle(blockIdx.x, total);
+  for (int i = tid; i < V; i += blockDim.x)
+    if (s_tab[i] * nt <= L && L < s_tab[i + 1] * nt) *s_v = i;
+  __syncthreads();
+  const int v = *s_v;
+  const int mt_v = s_tab[v + 1] - s_tab[v];
+  const int local = L - s_tab[v] * nt;
+  ti.v = v;
+  ti.n0 = (local / mt_v) * BNO;
+  ti.m0 = (local % mt_v) * BM;
+  ti.routed = v < a.N;
+  const int TK = a.T * a.K;
+  ti.row_base = 0;
+  ti.rows = a.T;
+  if (ti.routed) {
+    ti.row_base = min(max(a.offsets[v], 0), TK);
+    ti.rows = min(max(a.offsets[v + 1], ti.row_base), TK) - ti.row_base;
+  }
+  return true;
+}
+
+// Persistent kernels: load the tile table once, then map any tile id.
+template <int MODE>
+__device__ __forceinline__ int load_tile_table(const ExpertArgs& a, int* s_tab) {
+  const int V = MODE == 1 ? a.N + a.K_s : a.N + (a.K_s > 0 ? 1 : 0);
+  const int32_t* tab = MODE == 1 ? a.tiles1 : a.tiles2;
+  for (int i = threadIdx.x; i <= V; i += blockDim.x) s_tab[i] = tab[i];
+  __syncthreads();
+  return V;
+}
+
+// Tile L of the table in LDS (every thread searches the same entries: no barrier).
+template <int BM, int BNO, int MODE>
+__device__ __forceinline__ Tile tile_of(const ExpertArgs& a, const int* s_tab, int V, int L) {
+  const int nt = (MODE == 1 ? a.I : a.d) / BNO;
+  int lo = 0, hi = V - 1;  // largest v with s_tab[v] * nt <= L
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_tab[mid] * nt <= L) lo = mid; else hi = mid - 1;
+  }
+  // empty experts share their start with the next one: move to the first that owns L
+  while (lo + 1 <= V && s_tab[lo + 1] * nt <= L) ++lo;
+  Tile ti;
+  const int v = lo;
+  const int mt_v = s_tab[v + 1] - s_tab[v];
+  const int local = L - s_tab[v] * nt;
+  ti.v = v;
+  ti.n0 = (local / mt_v) * BNO;
+  ti.m0 = (local % mt_v) * BM;
+  ti.routed = v < a.N;
+  const int TK = a.T * a.K;
+  ti.row_base = 0;
+  ti.rows = a.T;
+  if (ti.routed) {
+    ti.row_base = min(max(a.offsets[v], 0), TK);
+    ti.rows = min(max(a.offsets[v + 1], ti.row_base), TK) - ti.row_base;
+  }
+  return ti;
+}
+
+// Start of tile row r (A rows 0..BM-1, then B rows) at contraction index 0.
+// A rows past the expert's last slot repeat its last row (never stored).
+template <class E, int MODE, int BM, int BNB>
+__device__ __forceinline__ const typename E::T* tile_row_ptr(const ExpertArgs& a, const Tile& ti,
+                                                             int r) {
+  using Tp = typename E::T;
+  const size_t Id = (size_t)a.I * a.d;
+  if (r < BM) {
+    const int p = min(ti.m0 + r, ti.rows - 1);
+    if (MODE == 1) {
+      int tok = p;
+      if (ti.routed) {
+        const int TK = a.T * a.K;
+        const int pair = a.sorted_pair[ti.row_base + p];
+        tok = ((unsigned)pair < (unsigned)TK) ? pair / a.K : 0;
+      }
+      return (const Tp*)a.u + (size_t)tok * a.d;
+    }
+    return ti.routed ? (const Tp*)a.H_routed + (size_t)(ti.row_base + p) * a.I
+                     : (const Tp*)a.H_shared + (size_t)p * a.K_s * a.I;
+  }
+  const int rb = r - BM;
+  const Tp* W = ti.routed ? (const Tp*)a.W_routed + (size_t)ti.v * 3 * Id
+                          : (const Tp*)a.W_shared + (size_t)(MODE == 1 ? ti.v - a.N : 0) * 3 * Id;
+  if (MODE == 1)
+    return rb < BNB / 2 ? W + (size_t)(ti.n0 + rb) * a.d
+                        : W + Id + (size_t)(ti.n0 + rb - BNB / 2) * a.d;
+  return W + 2 * Id + (size_t)(ti.n0 + rb) * a.I;
+}
+
+// Element offset of contraction index k0 in a B row.  The shared experts'
+// down projections are one contraction over K_s*I: index k0 lies in expert
+// k0 / I's W_down block.
+template <int MODE>
+__device__ __forceinline__ size_t b_offset(const ExpertArgs& a, const Tile& ti, size_t k0) {
+  if (MODE == 2 && !ti.routed) {
+    const size_t Id = (size_t)a.I * a.d;
+    return k0 + (k0 / a.I) * (3 * Id - a.I);
+  }
+  return k0;
+}
+
+// B tile row of wavefront column wn's fragment fn.  GEMM1 puts the gate rows
+// in the first half of the B tile and the up rows of the same columns in the
+// second half; a wavefront takes matching gate and up fragments.
+template <int MODE, int FN, int BNB>
+__device__ __forceinline__ int b_frag_row(int wn, int fn) {
+  if (MODE == 1)
+    return fn < FN / 2 ? (wn * (FN / 2) + fn) * 32
+                       : BNB / 2 + (wn * (FN / 2) + fn - FN / 2) * 32;
+  return (wn * FN + fn) * 32;
+}
+
+// Epilogue.  acc[fm][fn][r] holds tile row (wm*FM + fm)*32 + 8*(r/4) + 4*(lane/32) + r%4,
+// column lane%32 of fragment fn.
+template <class E, int MODE, int FM, int FN>
+__device__ __forceinline__ void store_tile(const ExpertArgs& a, const Tile& ti, int wm, int wn,
+                                           f32x16 (&acc)[FM][FN]) {
+  using Tp = typename E::T;
+  const int lane = threadIdx.x & 63;
+  const int lc = lane & 31, lh = lane >> 5;
+  const int TK = a.T * a.K;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int p = ti.m0 + (wm * FM + fm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (p >= ti.rows) continue;
+      if (MODE == 1) {
+#pragma unroll
+        for (int fn = 0; fn < FN / 2; ++fn) {
+          const float gt = acc[fm][fn][r], up = acc[fm][fn + FN / 2][r];
+          const float hv = gt / (1.f + expf(-gt)) * up;   // SiLU(gate) * up
+          const int col = ti.n0 + (wn * (FN / 2) + fn) * 32 + lc;
+          Tp* dst = ti.routed
+                        ? (Tp*)a.H_routed + (size_t)(ti.row_base + p) * a.I + col
+                        : (Tp*)a.H_shared + (size_t)p * a.K_s * a.I + (size_t)(ti.v - a.N) * a.I + col;
+          store_from_f32<E>(dst, hv);
+        }
+      } else {
+        float g = 1.f;
+        Tp* dst;
+        if (ti.routed) {
+          int pair = a.sorted_pair[ti.row_base + p];
+          pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
+          g = a.gate[pair];
+          dst = (Tp*)a.Y + (size_t)pair * a.d;
+        } else {
+          dst = (Tp*)a.Y_shared + (size_t)p * a.d;
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = ti.n0 + (wn * FN + fn) * 32 + lc;
+          store_from_f32<E>(dst + col, acc[fm][fn][r] * g);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- register-staged kernel
+// Any d, I that are multiples of 64: tiles staged global -> registers -> LDS,
+// two LDS buffers, up to two blocks per CU.
 template <class E, int WM, int WN, int FM, int FN, int MODE>
 __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
   using Tp = typename E::T;
   constexpr int BM = WM * FM * 32;
-  constexpr int BNB = WN * FN * 32;          // B rows per tile
+  constexpr int BNB = WN * FN * 32;               // B rows per tile
   constexpr int BNO = MODE == 1 ? BNB / 2 : BNB;  // output columns per tile
   constexpr int ROWS = BM + BNB;
   constexpr int PASSES = ROWS / 32;
@@ -101,71 +293,20 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int N = a.N, K = a.K, d = a.d, I = a.I, K_s = a.K_s, T = a.T;
-
-  // ---- which tile is this block's
-  const int V = MODE == 1 ? N + K_s : N + (K_s > 0 ? 1 : 0);
-  const int32_t* tab = MODE == 1 ? a.tiles1 : a.tiles2;
-  const int nt = (MODE == 1 ? I : d) / BNO;
-  for (int i = tid; i <= V; i += 256) s_tab[i] = tab[i];
-  __syncthreads();
-  const int L = xcd_swizzle(blockIdx.x, gridDim.x);
-  if (L >= s_tab[V] * nt) return;  // same decision in every thread of the block
-  for (int i = tid; i < V; i += 256)
-    if (s_tab[i] * nt <= L && L < s_tab[i + 1] * nt) s_v = i;
-  __syncthreads();
-  const int v = s_v;
-  const int mt_v = s_tab[v + 1] - s_tab[v];
-  const int local = L - s_tab[v] * nt;
-  const int n0 = (local / mt_v) * BNO;
-  const int m0 = (local % mt_v) * BM;
-  const bool routed = v < N;
-  const int TK = T * K;
-  int row_base = 0, rows = T;
-  if (routed) {
-    row_base = min(max(a.offsets[v], 0), TK);
-    rows = min(max(a.offsets[v + 1], row_base), TK) - row_base;
-  }
-  const size_t Id = (size_t)I * d;
-  const int Kc = MODE == 1 ? d : (routed ? I : K_s * I);  // contraction length
+  Tile ti;
+  if (!find_tile<BM, BNO, MODE>(a, s_tab, &s_v, ti)) return;
+  const int Kc = MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I);  // contraction length
   const int nsteps = Kc / kStep;
 
-  // ---- per-thread load rows (chunk c of rows tid/8 + 32 i)
+  // each thread moves chunk c of rows tid/8 + 32 i
   const int c = tid & 7;
   const Tp* rowp[PASSES];
 #pragma unroll
-  for (int i = 0; i < PASSES; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    if (i < PASSES_A) {
-      const int p = min(m0 + r, rows - 1);  // rows past the end repeat the last row
-      if (MODE == 1) {
-        int tok = p;
-        if (routed) {
-          const int pair = a.sorted_pair[row_base + p];
-          tok = ((unsigned)pair < (unsigned)TK) ? pair / K : 0;
-        }
-        rowp[i] = (const Tp*)a.u + (size_t)tok * d;
-      } else {
-        rowp[i] = routed ? (const Tp*)a.H_routed + (size_t)(row_base + p) * I
-                         : (const Tp*)a.H_shared + (size_t)p * K_s * I;
-      }
-    } else {
-      const int rb = r - BM;
-      const Tp* W = routed ? (const Tp*)a.W_routed + (size_t)v * 3 * Id
-                           : (const Tp*)a.W_shared + (size_t)(MODE == 1 ? v - N : 0) * 3 * Id;
-      if (MODE == 1) {
-        rowp[i] = rb < BNB / 2 ? W + (size_t)(n0 + rb) * d : W + Id + (size_t)(n0 + rb - BNB / 2) * d;
-      } else {
-        rowp[i] = W + 2 * Id + (size_t)(n0 + rb) * I;
-      }
-    }
-  }
-  // shared down projection: the k-step at k0 reads expert k0 / I's W_down
-  const bool shared_down = MODE == 2 && !routed;
+  for (int i = 0; i < PASSES; ++i) rowp[i] = tile_row_ptr<E, MODE, BM, BNB>(a, ti, (tid >> 3) + 32 * i);
   u32x4 stage[PASSES];
   auto gload = [&](int s) {
     const size_t k0 = (size_t)s * kStep;
-    const size_t kb = shared_down ? k0 + (k0 / I) * (3 * Id - I) : k0;
+    const size_t kb = b_offset<MODE>(a, ti, k0);
 #pragma unroll
     for (int i = 0; i < PASSES; ++i)
       stage[i] = *(const u32x4*)(rowp[i] + (i < PASSES_A ? k0 : kb) + c * E::kPerChunk);
@@ -174,11 +315,6 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
 #pragma unroll
     for (int i = 0; i < PASSES; ++i)
       *(u32x4*)(lds[buf] + lds_chunk_offset((tid >> 3) + 32 * i, c)) = stage[i];
-  };
-  auto brow = [&](int fn) {
-    if (MODE == 1)
-      return fn < FN / 2 ? (wn * (FN / 2) + fn) * 32 : BNB / 2 + (wn * (FN / 2) + fn - FN / 2) * 32;
-    return (wn * FN + fn) * 32;
   };
 
   f32x16 acc[FM][FN];
@@ -204,7 +340,8 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
         af[fm] = *(const u32x4*)(lds[buf] + lds_chunk_offset((wm * FM + fm) * 32 + (lane & 31), ch));
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        bfr[fn] = *(const u32x4*)(lds[buf] + lds_chunk_offset(BM + brow(fn) + (lane & 31), ch));
+        bfr[fn] = *(const u32x4*)(lds[buf] +
+                                  lds_chunk_offset(BM + b_frag_row<MODE, FN, BNB>(wn, fn) + (lane & 31), ch));
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -213,100 +350,429 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
     if (s + 1 < nsteps) lstore(buf ^ 1);
     __syncthreads();
   }
+  store_tile<E, MODE, FM, FN>(a, ti, wm, wn, acc);
+}
 
-  // ---- epilogue.  acc[fm][fn][r]: row 8*(r/4) + 4*(lane/32) + r%4, column lane%32.
-  const int lc = lane & 31, lh = lane >> 5;
+// ---------------------------------------------------------------- LDS-DMA kernel
+// Tiles of BM x 256 B rows, four wavefronts (2 x 2) of (BM/2) x 128 outputs.
+// Global -> LDS by direct-to-LDS loads (global_load_lds_dwordx4: lane L of a
+// wavefront writes 16 bytes at the wavefront's LDS address + 16 L) into a
+// ring of STAGES buffers, STAGES - 1 k-steps ahead, with explicit vmcnt
+// waits (the loads bypass registers, so the compiler cannot track them).
+// A k-step covers RB bytes of each row (128 or 64).  The LDS swizzle is
+// applied on the global side: lane L fetches the chunk that belongs in LDS
+// slot L.  MINB blocks share a CU.
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n)&0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+#define MOE_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14))
+
+// One k-step of the LDS-DMA kernel: refill ring slot `wr` with the loads of a
+// later k-step, then multiply out of slot `rd`.  The restrict qualifiers give
+// the compiler alias scopes, so it knows the refill never aliases the reads
+// and does not make the reads wait for it (the kernel's own vmcnt wait and
+// barrier order the refill of a slot after its last reads).
+template <int NINST>
+__device__ __forceinline__ void dma_fill(uint8_t* __restrict__ wr, const uint8_t* a_base,
+                                         const uint8_t* b_base, const uint32_t (&off)[NINST],
+                                         int n_a) {
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
+  for (int i = 0; i < NINST; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)((i < n_a ? a_base : b_base) + off[i]),
+                                     (__attribute__((address_space(3))) void*)(wr + i * 1024), 16,
+                                     0, 0);
+}
+
+template <int FM, int FN, int RB, int BM, int BNB, int MODE>
+__device__ __forceinline__ void load_frags(const uint8_t* __restrict__ rd, int kg, int wm, int wn,
+                                           int lane, u32x4 (&af)[FM], u32x4 (&bfr)[FN]) {
+  const int ch = kg * 2 + (lane >> 5);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = m0 + (wm * FM + fm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (p >= rows) continue;
-      if (MODE == 1) {
+  for (int fm = 0; fm < FM; ++fm)
+    af[fm] = *(const u32x4*)(rd + lds_chunk_offset_t<RB>((wm * FM + fm) * 32 + (lane & 31), ch));
 #pragma unroll
-        for (int fn = 0; fn < FN / 2; ++fn) {
-          const float gt = acc[fm][fn][r], up = acc[fm][fn + FN / 2][r];
-          const float hv = gt / (1.f + expf(-gt)) * up;
-          const int col = n0 + (wn * (FN / 2) + fn) * 32 + lc;
-          Tp* dst = routed ? (Tp*)a.H_routed + (size_t)(row_base + p) * I + col
-                           : (Tp*)a.H_shared + (size_t)p * K_s * I + (size_t)(v - N) * I + col;
-          store_from_f32<E>(dst, hv);
-        }
-      } else {
-        float g = 1.f;
-        Tp* dst;
-        if (routed) {
-          int pair = a.sorted_pair[row_base + p];
-          pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
-          g = a.gate[pair];
-          dst = (Tp*)a.Y + (size_t)pair * d;
-        } else {
-          dst = (Tp*)a.Y_shared + (size_t)p * d;
-        }
+  for (int fn = 0; fn < FN; ++fn)
+    bfr[fn] = *(const u32x4*)(rd + lds_chunk_offset_t<RB>(
+                                       BM + b_frag_row<MODE, FN, BNB>(wn, fn) + (lane & 31), ch));
+}
+
+// One k-step of the LDS-DMA kernel: refill ring slot `wr` with the loads of a
+// later k-step, then multiply out of slot `rd`, reading the fragments of the
+// next 16-k group while the current one is on the MFMA pipe.  The restrict
+// qualifiers give the compiler alias scopes, so it knows the refill never
+// aliases the reads and does not make the reads wait for it (the kernel's own
+// vmcnt wait and barrier order the refill of a slot after its last reads).
+template <class E, int NINST, int KG, int FM, int FN, int RB, int BM, int BNB, int MODE>
+__device__ __forceinline__ void dma_kstep(const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr,
+                                          const uint8_t* a_base, const uint8_t* b_base,
+                                          const uint32_t (&off)[NINST], int n_a, bool active,
+                                          int wm, int wn, int lane, f32x16 (&acc)[FM][FN]) {
+  dma_fill<NINST>(wr, a_base, b_base, off, n_a);
+  if (!active) return;  // all of this wavefront's rows lie past the expert's last slot
+  u32x4 af[2][FM], bfr[2][FN];
+  load_frags<FM, FN, RB, BM, BNB, MODE>(rd, 0, wm, wn, lane, af[0], bfr[0]);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int col = n0 + (wn * FN + fn) * 32 + lc;
-          store_from_f32<E>(dst + col, acc[fm][fn][r] * g);
-        }
-      }
-    }
+  for (int kg = 0; kg < KG; ++kg) {
+    if (kg + 1 < KG)
+      load_frags<FM, FN, RB, BM, BNB, MODE>(rd, kg + 1, wm, wn, lane, af[(kg + 1) & 1],
+                                            bfr[(kg + 1) & 1]);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = mfma32(E{}, af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
   }
 }
 
-// Tile shapes (wavefronts WM x WN, 32x32 fragments FM x FN per wavefront).
+// bfloat16 epilogue staged through LDS: the wavefronts write their (gated,
+// SwiGLU'd) results as bf16 into a row-major tile in LDS (16-byte chunks
+// XOR-swizzled by row), then every thread copies whole 16-byte chunks of rows
+// to global memory, so each row leaves as full contiguous segments.
+template <int MODE, int FM, int FN, int BM, int NTHREADS>
+__device__ __forceinline__ void store_tile_bf16_lds(const ExpertArgs& a, const Tile& ti, int wm,
+                                                    int wn, f32x16 (&acc)[FM][FN],
+                                                    uint8_t* __restrict__ stage) {
+  constexpr int COLS = 128;                 // columns staged per pass
+  constexpr int CPRW = COLS * 2 / 16;       // 16-byte chunks per staged row (16)
+  constexpr int PASSES = MODE == 1 ? 1 : 2; // GEMM2 tiles are 256 wide: two halves
+  const int lane = threadIdx.x & 63, lc = lane & 31, lh = lane >> 5;
+  const int TK = a.T * a.K;
+  auto lds_off = [&](int row, int col) {   // byte offset of element (row, col) in the stage
+    const int c = col >> 3;
+    return row * (COLS * 2) + (((c ^ (row & 7)) << 4) | ((col & 7) << 1));
+  };
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    // ---- registers -> LDS
+    if (MODE == 1 || wn == pass) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = (wm * FM + fm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          float g = 1.f;
+          if (MODE == 2 && ti.routed) {
+            const int p = min(ti.m0 + row, ti.rows - 1);
+            int pair = a.sorted_pair[ti.row_base + p];
+            pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
+            g = a.gate[pair];
+          }
+          if (MODE == 1) {
+#pragma unroll
+            for (int fn = 0; fn < FN / 2; ++fn) {
+              const float gt = acc[fm][fn][r], up = acc[fm][fn + FN / 2][r];
+              const float hv = gt / (1.f + expf(-gt)) * up;   // SiLU(gate) * up
+              const int col = (wn * (FN / 2) + fn) * 32 + lc;
+              *(uint16_t*)(stage + lds_off(row, col)) = f32_to_bf16(hv);
+            }
+          } else {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+              const int col = fn * 32 + lc;
+              *(uint16_t*)(stage + lds_off(row, col)) = f32_to_bf16(acc[fm][fn][r] * g);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- LDS -> global, 16 bytes per thread per chunk
+    for (int i = threadIdx.x; i < BM * CPRW; i += NTHREADS) {
+      const int row = i / CPRW, c = i % CPRW;
+      const int p = ti.m0 + row;
+      if (p >= ti.rows) continue;
+      const u32x4 v = *(const u32x4*)(stage + row * (COLS * 2) + ((c ^ (row & 7)) << 4));
+      uint16_t* dst;
+      if (MODE == 1) {
+        dst = ti.routed ? (uint16_t*)a.H_routed + (size_t)(ti.row_base + p) * a.I
+                        : (uint16_t*)a.H_shared + (size_t)p * a.K_s * a.I + (size_t)(ti.v - a.N) * a.I;
+        dst += ti.n0 + c * 8;
+      } else {
+        if (ti.routed) {
+          int pair = a.sorted_pair[ti.row_base + p];
+          pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
+          dst = (uint16_t*)a.Y + (size_t)pair * a.d;
+        } else {
+          dst = (uint16_t*)a.Y_shared + (size_t)p * a.d;
+        }
+        dst += ti.n0 + pass * COLS + c * 8;
+      }
+      *(u32x4*)dst = v;
+    }
+    __syncthreads();
+  }
+}
+
+template <class E, int WM, int RB, int STAGES, int MINB, int MODE>
+__global__ __launch_bounds__(WM * 128, MINB) void expert_gemm_dma_kernel(ExpertArgs a) {
+  using Tp = typename E::T;
+  constexpr int WN = 2, NWAVES = WM * WN;
+  constexpr int FM = 2, FN = 4;                // each wavefront: 64 rows x 128 columns
+  constexpr int BM = WM * FM * 32;
+  constexpr int BNB = 256;
+  constexpr int BNO = MODE == 1 ? BNB / 2 : BNB;
+  constexpr int ROWS = BM + BNB;
+  constexpr int CPR = RB / 16;                 // 16-byte chunks per row and k-step
+  constexpr int RPI = 64 / CPR;                // rows one wavefront load covers
+  constexpr int STAGE_BYTES = ROWS * RB;
+  constexpr int NINST = ROWS / (NWAVES * RPI); // loads per wavefront per stage
+  constexpr int kStep = RB / (int)sizeof(Tp);  // contraction elements per k-step
+  constexpr int KG = RB / 32;                  // 16-k groups per k-step (2 chunks each)
+  static_assert(RB == 64 || RB == 128, "row bytes");
+  static_assert(STAGES >= 2 && STAGES * STAGE_BYTES * MINB <= 152 * 1024, "LDS budget");
+  static_assert((STAGES - 2) * NINST <= 63, "vmcnt range");
+  // One array per ring slot, always addressed through a compile-time slot
+  // number: the compiler then knows that the direct-to-LDS loads filling one
+  // slot never alias the reads of another and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGES > 2 ? STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[STAGES > 3 ? STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds4[STAGES > 4 ? STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds5[STAGES > 5 ? STAGE_BYTES : 16];
+  static_assert(STAGES <= 6, "ring slots");
+  __shared__ int s_tab[kMaxV + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  auto slot = [&](auto U) -> uint8_t* {
+    constexpr int u = decltype(U)::value;
+    if constexpr (u == 0) return lds0;
+    else if constexpr (u == 1) return lds1;
+    else if constexpr (u == 2) return lds2;
+    else if constexpr (u == 3) return lds3;
+    else if constexpr (u == 4) return lds4;
+    else return lds5;
+  };
+
+  // Persistent: the blocks of XCD x (blockIdx % 8, workgroups are dealt
+  // round-robin over the XCDs) walk that XCD's contiguous range of tiles in
+  // rounds, so the tiles of one round share an expert's weights and tokens in
+  // the XCD's L2 and move through the contraction together.
+  const int V = load_tile_table<MODE>(a, s_tab);
+  const int total = s_tab[V] * ((MODE == 1 ? a.I : a.d) / BNO);
+  const int X = min(8, (int)gridDim.x);  // groups (XCDs) that have blocks
+  const int x = blockIdx.x % X, lb = blockIdx.x / X;
+  const int nbx = ((int)gridDim.x - x + X - 1) / X;
+  const int q = total / X, rem = total % X;
+  const int start = x * q + min(x, rem), end = start + q + (x < rem ? 1 : 0);
+  for (int L = start + lb; L < end; L += nbx) {
+  const Tile ti = tile_of<BM, BNO, MODE>(a, s_tab, V, L);
+  const int Kc = MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I);
+  const int nsteps = Kc / kStep;
+  const bool wave_active = ti.m0 + wm * FM * 32 < ti.rows;
+  // the previous tile's stores have left and every wavefront is done with the ring
+  MOE_WAIT_VMCNT(0);
+  MOE_WAIT_LGKMCNT0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // Row groups q = wave*NINST + i (RPI rows each); lane -> row q*RPI + lane/CPR,
+  // slot lane%CPR, which holds chunk slot ^ swizzle(row).  Each lane keeps a
+  // 32-bit byte offset from the A operand's base (u or H) or the B operand's
+  // base (the expert's weight block); the bases are wavefront-uniform.
+  const uint8_t* a0 = (const uint8_t*)tile_row_ptr<E, MODE, BM, BNB>(a, ti, BM) ;  // B row 0
+  const uint8_t* a_base = MODE == 1 ? (const uint8_t*)a.u
+                                    : (const uint8_t*)(ti.routed ? a.H_routed : a.H_shared);
+  uint32_t off[NINST];
+#pragma unroll
+  for (int i = 0; i < NINST; ++i) {
+    const int r = (wave * NINST + i) * RPI + lane / CPR;
+    const uint8_t* rp = (const uint8_t*)tile_row_ptr<E, MODE, BM, BNB>(a, ti, r);
+    const int slot = lane % CPR;
+    const int chunk = RB == 128 ? (slot ^ ((r >> 1) & 7)) : (slot ^ ((r >> 2) & 3));
+    off[i] = (uint32_t)(rp - (r < BM ? a_base : a0)) + chunk * 16;
+  }
+  const int n_a = min(max(BM / RPI - wave * NINST, 0), NINST);  // this wavefront's A-row loads
+  auto bases = [&](int s, const uint8_t*& ab, const uint8_t*& bb) {
+    const size_t k0 = (size_t)s * kStep;
+    ab = a_base + k0 * sizeof(Tp);
+    bb = a0 + b_offset<MODE>(a, ti, k0) * sizeof(Tp);
+  };
+  auto issue = [&](auto U, int s) {  // k-step s into ring slot U
+    const uint8_t *ab, *bb;
+    bases(s, ab, bb);
+    dma_fill<NINST>(slot(U) + wave * NINST * 1024, ab, bb, off, n_a);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  // prologue: k-steps 0 .. STAGES-2 into slots 0 .. STAGES-2.  Loads are
+  // issued unconditionally (k-steps past the end repeat the last one into a
+  // slot nobody reads), so every step waits for the same count.
+  const int last = nsteps - 1;
+  issue(I0{}, 0);
+  if constexpr (STAGES > 2) issue(I1{}, min(1, last));
+  if constexpr (STAGES > 3) issue(I2{}, min(2, last));
+  if constexpr (STAGES > 4) issue(I3{}, min(3, last));
+  if constexpr (STAGES > 5) issue(I4{}, min(4, last));
+
+  // k-step s reads slot s % STAGES and refills slot (s - 1) % STAGES with k-step s + STAGES - 1
+  auto step = [&](auto U, int s) {
+    constexpr int u = decltype(U)::value;
+    using W = std::integral_constant<int, (u + STAGES - 1) % STAGES>;
+    // stage s has landed once only the STAGES-2 later stages are in flight
+    MOE_WAIT_VMCNT((STAGES - 2) * NINST);
+    MOE_WAIT_LGKMCNT0();  // this wavefront's reads of the slot about to be refilled are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    const uint8_t *ab, *bb;
+    bases(min(s + STAGES - 1, last), ab, bb);
+    dma_kstep<E, NINST, KG, FM, FN, RB, BM, BNB, MODE>(slot(U), slot(W{}) + wave * NINST * 1024,
+                                                       ab, bb, off, n_a, wave_active, wm, wn,
+                                                       lane, acc);
+  };
+  for (int s0 = 0; s0 < nsteps; s0 += STAGES) {
+    step(I0{}, s0);
+    if (s0 + 1 < nsteps) step(I1{}, s0 + 1);
+    if constexpr (STAGES > 2) if (s0 + 2 < nsteps) step(I2{}, s0 + 2);
+    if constexpr (STAGES > 3) if (s0 + 3 < nsteps) step(I3{}, s0 + 3);
+    if constexpr (STAGES > 4) if (s0 + 4 < nsteps) step(I4{}, s0 + 4);
+    if constexpr (STAGES > 5) if (s0 + 5 < nsteps) step(I5{}, s0 + 5);
+  }
+  if constexpr (std::is_same<E, ElemBF16>::value && STAGE_BYTES >= BM * 256) {
+    // the ring is free once every wavefront has finished its last reads
+    MOE_WAIT_VMCNT(0);
+    MOE_WAIT_LGKMCNT0();
+    __syncthreads();
+    store_tile_bf16_lds<MODE, FM, FN, BM, WM * 128>(a, ti, wm, wn, acc, lds0);
+  } else {
+    store_tile<E, MODE, FM, FN>(a, ti, wm, wn, acc);
+  }
+  }
+}
+
+// Kernel variants.  kind 0: register-staged kernel with wavefronts WM x WN and
+// 32x32 fragments FM x FN per wavefront.  kind 1: LDS-DMA kernel with
+// BM x 256 tiles (FM = BM / 64), rb bytes per row per k-step, `stages` LDS
+// buffers and minb blocks per CU.
 struct Shape {
-  int WM, WN, FM, FN;
-  int bm() const { return WM * FM * 32; }
-  int bnb() const { return WN * FN * 32; }
+  int kind, WM, WN, FM, FN, stages, rb, minb;
+  int bm() const { return kind == 1 ? FM * 64 : WM * FM * 32; }
 };
 
 // Few tokens per expert (decode-sized batches): short M tiles, wide N tiles,
-// so every CU streams a large weight slab.  Otherwise 128x128 tiles.
+// so every CU streams a large weight slab.
 bool small_m(const ExpertArgs& a) { return (long long)a.T * a.K < 64LL * a.N; }
 
-Shape shape1(const ExpertArgs& a) {
-  if (small_m(a)) return a.I % 128 == 0 ? Shape{1, 4, 1, 2} : Shape{2, 2, 1, 2};
-  return Shape{2, 2, 2, 2};
-}
-Shape shape2(const ExpertArgs& a) {
-  if (small_m(a)) return a.d % 256 == 0 ? Shape{1, 4, 1, 2} : Shape{2, 2, 1, 1};
-  return a.d % 128 == 0 ? Shape{2, 2, 2, 2} : Shape{2, 2, 2, 1};
+// Tuning override, read once:
+// MOE_GEMM_VARIANT = reg | dma128 | dma256k32 | dma128k32 | dma128k32x6 | dma256
+int variant_override() {
+  static int v = [] {
+    const char* e = getenv("MOE_GEMM_VARIANT");
+    if (e == nullptr) return -1;
+    const char* names[] = {"reg", "dma128", "dma256k32", "dma128k32", "dma128k32x6", "dma256"};
+    for (int i = 0; i < 6; ++i)
+      if (!strcmp(e, names[i])) return i;
+    return -1;
+  }();
+  return v;
 }
 
-long long grid_tiles(const ExpertArgs& a, int bm, int nt, int shared_mtiles) {
+constexpr int kDefaultVariant = 5;
+
+Shape dma_shape(int variant) {
+  switch (variant) {
+    case 2: return Shape{1, 4, 2, 4, 4, 4, 64, 1};    // 256 x 256, 8 wavefronts, 4 x 32 KB
+    case 3: return Shape{1, 2, 2, 2, 4, 3, 64, 2};    // 128 x 256, 3 x 24 KB, 2 blocks/CU
+    case 4: return Shape{1, 2, 2, 2, 4, 6, 64, 1};    // 128 x 256, 6 x 24 KB
+    case 5: return Shape{1, 4, 2, 4, 4, 2, 128, 1};   // 256 x 256, 8 wavefronts, 2 x 64 KB
+    default: return Shape{1, 2, 2, 2, 4, 3, 128, 1};  // 128 x 256, 3 x 48 KB
+  }
+}
+
+Shape shape1(const ExpertArgs& a) {
+  if (small_m(a)) return a.I % 128 == 0 ? Shape{0, 1, 4, 1, 2, 2, 128, 2} : Shape{0, 2, 2, 1, 2, 2, 128, 2};
+  const int ov = variant_override();
+  if (a.I % 128 == 0 && ov != 0) return dma_shape(ov < 0 ? kDefaultVariant : ov);
+  return Shape{0, 2, 2, 2, 2, 2, 128, 2};
+}
+Shape shape2(const ExpertArgs& a) {
+  if (small_m(a)) return a.d % 256 == 0 ? Shape{0, 1, 4, 1, 2, 2, 128, 2} : Shape{0, 2, 2, 1, 1, 2, 128, 2};
+  const int ov = variant_override();
+  if (a.d % 256 == 0 && ov != 0) return dma_shape(ov < 0 ? kDefaultVariant : ov);
+  return a.d % 128 == 0 ? Shape{0, 2, 2, 2, 2, 2, 128, 2} : Shape{0, 2, 2, 2, 1, 2, 128, 2};
+}
+
+long long grid_tiles(const ExpertArgs& a, int bm, int nt, int mode) {
   const long long routed = ((long long)a.T * a.K + (long long)a.N * (bm - 1)) / bm;
-  return (routed + shared_mtiles) * nt;
+  const long long mtT = (a.T + bm - 1) / bm;
+  const long long shared = mode == 1 ? a.K_s * mtT : (a.K_s > 0 ? mtT : 0);
+  return (routed + shared) * nt;
 }
 
 template <class E, int WM, int WN, int FM, int FN, int MODE>
-hipError_t launch_one(const ExpertArgs& a, hipStream_t st) {
+hipError_t launch_reg(const ExpertArgs& a, hipStream_t st) {
   constexpr int BM = WM * FM * 32;
   constexpr int BNO = MODE == 1 ? WN * FN * 16 : WN * FN * 32;
-  const int nt = (MODE == 1 ? a.I : a.d) / BNO;
-  const int mtT = (a.T + BM - 1) / BM;
-  const int shared_mt = MODE == 1 ? a.K_s * mtT : (a.K_s > 0 ? mtT : 0);
-  const long long g = grid_tiles(a, BM, nt, shared_mt);
+  const long long g = grid_tiles(a, BM, (MODE == 1 ? a.I : a.d) / BNO, MODE);
   if (g <= 0) return hipSuccess;
   if (g > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   expert_gemm_kernel<E, WM, WN, FM, FN, MODE><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <class E>
-hipError_t launch_gemm1_t(const ExpertArgs& a, hipStream_t st) {
-  const Shape s = shape1(a);
-  if (s.WM == 1) return launch_one<E, 1, 4, 1, 2, 1>(a, st);
-  if (s.FM == 1) return launch_one<E, 2, 2, 1, 2, 1>(a, st);
-  return launch_one<E, 2, 2, 2, 2, 1>(a, st);
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
-template <class E>
-hipError_t launch_gemm2_t(const ExpertArgs& a, hipStream_t st) {
-  const Shape s = shape2(a);
-  if (s.WM == 1) return launch_one<E, 1, 4, 1, 2, 2>(a, st);
-  if (s.FM == 1) return launch_one<E, 2, 2, 1, 1, 2>(a, st);
-  if (s.FN == 2) return launch_one<E, 2, 2, 2, 2, 2>(a, st);
-  return launch_one<E, 2, 2, 2, 1, 2>(a, st);
+template <class E, int WM, int RB, int STAGES, int MINB, int MODE>
+hipError_t launch_dma(const ExpertArgs& a, hipStream_t st) {
+  constexpr int BM = WM * 64;
+  constexpr int BNO = MODE == 1 ? 128 : 256;
+  long long g = grid_tiles(a, BM, (MODE == 1 ? a.I : a.d) / BNO, MODE);
+  if (g <= 0) return hipSuccess;
+  g = std::min<long long>(g, (long long)cu_count() * MINB);  // persistent: one block per slot
+  expert_gemm_dma_kernel<E, WM, RB, STAGES, MINB, MODE>
+      <<<dim3((unsigned)g), dim3(WM * 128), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <class E, int MODE>
+hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
+  const Shape s = MODE == 1 ? shape1(a) : shape2(a);
+  if (s.kind == 1) {
+    if (s.FM == 4 && s.rb == 128) return launch_dma<E, 4, 128, 2, 1, MODE>(a, st);
+    if (s.FM == 4) return launch_dma<E, 4, 64, 4, 1, MODE>(a, st);
+    if (s.rb == 64 && s.minb == 2) return launch_dma<E, 2, 64, 3, 2, MODE>(a, st);
+    if (s.rb == 64) return launch_dma<E, 2, 64, 6, 1, MODE>(a, st);
+    return launch_dma<E, 2, 128, 3, 1, MODE>(a, st);
+  }
+  if (MODE == 1) {
+    if (s.WM == 1) return launch_reg<E, 1, 4, 1, 2, 1>(a, st);
+    if (s.FM == 1) return launch_reg<E, 2, 2, 1, 2, 1>(a, st);
+    return launch_reg<E, 2, 2, 2, 2, 1>(a, st);
+  }
+  if (s.WM == 1) return launch_reg<E, 1, 4, 1, 2, 2>(a, st);
+  if (s.FM == 1) return launch_reg<E, 2, 2, 1, 1, 2>(a, st);
+  if (s.FN == 2) return launch_reg<E, 2, 2, 2, 2, 2>(a, st);
+  return launch_reg<E, 2, 2, 2, 1, 2>(a, st);
 }
 
 }  // namespace
@@ -321,11 +787,11 @@ hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream)
 }
 
 hipError_t launch_gemm1(int dtype, const ExpertArgs& a, hipStream_t stream) {
-  return dtype == 1 ? launch_gemm1_t<ElemBF16>(a, stream) : launch_gemm1_t<ElemF32>(a, stream);
+  return dtype == 1 ? launch_mode<ElemBF16, 1>(a, stream) : launch_mode<ElemF32, 1>(a, stream);
 }
 
 hipError_t launch_gemm2(int dtype, const ExpertArgs& a, hipStream_t stream) {
-  return dtype == 1 ? launch_gemm2_t<ElemBF16>(a, stream) : launch_gemm2_t<ElemF32>(a, stream);
+  return dtype == 1 ? launch_mode<ElemBF16, 2>(a, stream) : launch_mode<ElemF32, 2>(a, stream);
 }
 
 }  // namespace moe

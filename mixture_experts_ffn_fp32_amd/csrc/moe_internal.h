@@ -59,6 +59,13 @@ __device__ __forceinline__ void store_from_f32<ElemBF16>(uint16_t* p, float v) {
 __device__ __forceinline__ int lds_chunk_offset(int r, int c) {
   return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
 }
+// The same for 64-byte rows (4 chunks): four rows share a 256-byte bank
+// window, so chunk c of row r lives at slot c ^ ((r >> 2) & 3).
+template <int ROW_BYTES>
+__device__ __forceinline__ int lds_chunk_offset_t(int r, int c) {
+  if (ROW_BYTES == 128) return lds_chunk_offset(r, c);
+  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
 
 // ---------------------------------------------------------------- launchers
 // Router: logits, softmax, top-K.  Returns hipError_t of the launch.

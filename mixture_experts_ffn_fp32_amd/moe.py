@@ -11,7 +11,8 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 NUM_STAGES = 7
