@@ -353,24 +353,15 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
   store_tile<E, MODE, FM, FN>(a, ti, wm, wn, acc);
 }
 
-// ---------------------------------------------------------------- LDS-DMA kernel
-// Tiles of BM x 256 B rows, four wavefronts (2 x 2) of (BM/2) x 128 outputs.
-// Global -> LDS by direct-to-LDS loads (global_load_lds_dwordx4: lane L of a
-// wavefront writes 16 bytes at the wavefront's LDS address + 16 L) into a
-// ring of STAGES buffers, STAGES - 1 k-steps ahead, with explicit vmcnt
-// waits (the loads bypass registers, so the compiler cannot track them).
-// A k-step covers RB bytes of each row (128 or 64).  The LDS swizzle is
-// applied on the global side: lane L fetches the chunk that belongs in LDS
-// slot L.  MINB blocks share a CU.
+// ---------------------------------------------------------------- LDS-DMA helpers
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n)&0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
 #define MOE_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14))
 
-// One k-step of the LDS-DMA kernel: refill ring slot `wr` with the loads of a
-// later k-step, then multiply out of slot `rd`.  The restrict qualifiers give
-// the compiler alias scopes, so it knows the refill never aliases the reads
-// and does not make the reads wait for it (the kernel's own vmcnt wait and
-// barrier order the refill of a slot after its last reads).
+// Direct-to-LDS loads of one k-step of this lane's rows into `wr`.  The
+// restrict qualifier gives the compiler an alias scope, so it never makes LDS
+// reads of the other ring slot wait for these loads (the kernel orders the
+// refill of a slot after its last reads with its own waits and barrier).
 template <int NINST>
 __device__ __forceinline__ void dma_fill(uint8_t* __restrict__ wr, const uint8_t* a_base,
                                          const uint8_t* b_base, const uint32_t (&off)[NINST],
@@ -395,26 +386,87 @@ __device__ __forceinline__ void load_frags(const uint8_t* __restrict__ rd, int k
                                        BM + b_frag_row<MODE, FN, BNB>(wn, fn) + (lane & 31), ch));
 }
 
-// One k-step of the LDS-DMA kernel: refill ring slot `wr` with the loads of a
-// later k-step, then multiply out of slot `rd`, reading the fragments of the
-// next 16-k group while the current one is on the MFMA pipe.  The restrict
-// qualifiers give the compiler alias scopes, so it knows the refill never
-// aliases the reads and does not make the reads wait for it (the kernel's own
-// vmcnt wait and barrier order the refill of a slot after its last reads).
-template <class E, int NINST, int KG, int FM, int FN, int RB, int BM, int BNB, int MODE>
-__device__ __forceinline__ void dma_kstep(const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr,
-                                          const uint8_t* a_base, const uint8_t* b_base,
-                                          const uint32_t (&off)[NINST], int n_a, bool active,
-                                          int wm, int wn, int lane, f32x16 (&acc)[FM][FN]) {
-  dma_fill<NINST>(wr, a_base, b_base, off, n_a);
-  if (!active) return;  // all of this wavefront's rows lie past the expert's last slot
+// ---------------------------------------------------------------- pipelined LDS-DMA kernel
+// Tiles of 256 rows x 256 B rows (GEMM1: 128 gate + 128 up rows of the same
+// columns; GEMM2: 256 output columns), eight wavefronts (4 x 2), each owning
+// 64 rows x 128 columns (2 x 4 fragments of 32 x 32).  Operands reach LDS by
+// direct-to-LDS loads (global_load_lds_dwordx4: lane L of a wavefront writes
+// 16 bytes at the wavefront's LDS address + 16 L), one 128-byte k-step per
+// row, in a two-slot ring: k-step s + 1 lands while k-step s is multiplied.
+// The LDS swizzle is applied on the global side (lane L fetches the chunk that
+// belongs in LDS slot L).  The kernel is persistent; while a tile's results
+// are written out (staged through the free ring slot as bf16 rows), the next
+// tile's first k-step is already loading.  One block per CU.
+constexpr int kPipeBM = 256, kPipeBNB = 256, kPipeRB = 128, kPipeThreads = 512;
+constexpr int kPipeSlot = (kPipeBM + kPipeBNB) * kPipeRB;  // 64 KB
+constexpr int kPipeNinst = (kPipeBM + kPipeBNB) / (8 * 8);  // loads per wavefront per k-step
+
+// Per-tile load state of one lane: operand bases and 32-bit byte offsets.
+struct PipeLoads {
+  const uint8_t* a_base;     // u (GEMM1) or H (GEMM2) at contraction index 0
+  const uint8_t* b_row0;     // the tile's first B row at contraction index 0
+  uint32_t off[kPipeNinst];  // this lane's chunk of each of its rows
+};
+
+// Keeps a wavefront-uniform value in a scalar register.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const uint8_t* uni(const uint8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ Tile uni(const Tile& t) {
+  Tile u;
+  u.v = uni(t.v);
+  u.n0 = uni(t.n0);
+  u.m0 = uni(t.m0);
+  u.row_base = uni(t.row_base);
+  u.rows = uni(t.rows);
+  u.routed = uni((int)t.routed) != 0;
+  return u;
+}
+
+template <class E, int MODE>
+__device__ __forceinline__ void pipe_prepare(const ExpertArgs& a, const Tile& ti, int wave,
+                                             int lane, PipeLoads& ld) {
+  ld.b_row0 = uni((const uint8_t*)tile_row_ptr<E, MODE, kPipeBM, kPipeBNB>(a, ti, kPipeBM));
+  ld.a_base = uni(MODE == 1 ? (const uint8_t*)a.u
+                            : (const uint8_t*)(ti.routed ? a.H_routed : a.H_shared));
+#pragma unroll
+  for (int i = 0; i < kPipeNinst; ++i) {
+    const int r = (wave * kPipeNinst + i) * 8 + (lane >> 3);
+    const uint8_t* rp = (const uint8_t*)tile_row_ptr<E, MODE, kPipeBM, kPipeBNB>(a, ti, r);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    ld.off[i] = (uint32_t)(rp - (r < kPipeBM ? ld.a_base : ld.b_row0)) + chunk * 16;
+  }
+}
+
+template <class E, int MODE>
+__device__ __forceinline__ void pipe_issue(const ExpertArgs& a, const Tile& ti,
+                                           const PipeLoads& ld, int s, int n_a,
+                                           uint8_t* __restrict__ wr) {
+  using Tp = typename E::T;
+  constexpr int kStep = kPipeRB / (int)sizeof(Tp);
+  const size_t k0 = (size_t)s * kStep;
+  const uint8_t* ab = ld.a_base + k0 * sizeof(Tp);
+  const uint8_t* bb = ld.b_row0 + b_offset<MODE>(a, ti, k0) * sizeof(Tp);
+  dma_fill<kPipeNinst>(wr, ab, bb, ld.off, n_a);
+}
+
+// Multiplies one k-step out of slot `rd` (fragments of the next 16-k group are
+// read while the current one is on the MFMA pipe).
+template <class E, int MODE>
+__device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm, int wn, int lane,
+                                         f32x16 (&acc)[2][4]) {
+  constexpr int FM = 2, FN = 4, KG = kPipeRB / 32;
   u32x4 af[2][FM], bfr[2][FN];
-  load_frags<FM, FN, RB, BM, BNB, MODE>(rd, 0, wm, wn, lane, af[0], bfr[0]);
+  load_frags<FM, FN, kPipeRB, kPipeBM, kPipeBNB, MODE>(rd, 0, wm, wn, lane, af[0], bfr[0]);
 #pragma unroll
   for (int kg = 0; kg < KG; ++kg) {
     if (kg + 1 < KG)
-      load_frags<FM, FN, RB, BM, BNB, MODE>(rd, kg + 1, wm, wn, lane, af[(kg + 1) & 1],
-                                            bfr[(kg + 1) & 1]);
+      load_frags<FM, FN, kPipeRB, kPipeBM, kPipeBNB, MODE>(rd, kg + 1, wm, wn, lane,
+                                                            af[(kg + 1) & 1], bfr[(kg + 1) & 1]);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -423,291 +475,243 @@ __device__ __forceinline__ void dma_kstep(const uint8_t* __restrict__ rd, uint8_
   }
 }
 
-// bfloat16 epilogue staged through LDS: the wavefronts write their (gated,
-// SwiGLU'd) results as bf16 into a row-major tile in LDS (16-byte chunks
-// XOR-swizzled by row), then every thread copies whole 16-byte chunks of rows
-// to global memory, so each row leaves as full contiguous segments.
-template <int MODE, int FM, int FN, int BM, int NTHREADS>
-__device__ __forceinline__ void store_tile_bf16_lds(const ExpertArgs& a, const Tile& ti, int wm,
-                                                    int wn, f32x16 (&acc)[FM][FN],
-                                                    uint8_t* __restrict__ stage) {
-  constexpr int COLS = 128;                 // columns staged per pass
-  constexpr int CPRW = COLS * 2 / 16;       // 16-byte chunks per staged row (16)
-  constexpr int PASSES = MODE == 1 ? 1 : 2; // GEMM2 tiles are 256 wide: two halves
+// s_waitcnt vmcnt(0) lgkmcnt(0), then a barrier without memory fences (the
+// direct-to-LDS loads are ordered by the explicit wait instead).
+__device__ __forceinline__ void pipe_sync() {
+  MOE_WAIT_VMCNT(0);
+  MOE_WAIT_LGKMCNT0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// LDS-only synchronisation: this wavefront's LDS operations are done, then a
+// barrier.  Direct-to-LDS loads still in flight (into the other ring slot)
+// are not waited for.
+__device__ __forceinline__ void lds_sync() {
+  MOE_WAIT_LGKMCNT0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// SiLU(g) * u with the hardware exp2 and reciprocal (a few float32 ulp).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
+// Epilogue through LDS: the wavefronts write their results as bf16 into a
+// row-major staging tile (16-byte chunks XOR-swizzled by row), then every
+// thread copies whole 16-byte row chunks to global memory.  GEMM2 tiles are
+// 256 columns wide and go out in two halves.  s_dst[r] is the destination
+// row of tile row r (-1: past the expert's last slot), s_gate[r] its gate.
+template <int MODE>
+__device__ __forceinline__ void pipe_store_bf16(const ExpertArgs& a, const Tile& ti, int wm, int wn,
+                                                f32x16 (&acc)[2][4], uint8_t* __restrict__ stage,
+                                                const int* s_dst, const float* s_gate) {
+  constexpr int FM = 2, FN = 4, COLS = 128, CPRW = COLS * 2 / 16;
+  constexpr int PASSES = MODE == 1 ? 1 : 2;
   const int lane = threadIdx.x & 63, lc = lane & 31, lh = lane >> 5;
-  const int TK = a.T * a.K;
-  auto lds_off = [&](int row, int col) {   // byte offset of element (row, col) in the stage
+  auto lds_off = [&](int row, int col) {
     const int c = col >> 3;
     return row * (COLS * 2) + (((c ^ (row & 7)) << 4) | ((col & 7) << 1));
   };
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
-    // ---- registers -> LDS
     if (MODE == 1 || wn == pass) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = (wm * FM + fm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          float g = 1.f;
-          if (MODE == 2 && ti.routed) {
-            const int p = min(ti.m0 + row, ti.rows - 1);
-            int pair = a.sorted_pair[ti.row_base + p];
-            pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
-            g = a.gate[pair];
-          }
           if (MODE == 1) {
 #pragma unroll
             for (int fn = 0; fn < FN / 2; ++fn) {
-              const float gt = acc[fm][fn][r], up = acc[fm][fn + FN / 2][r];
-              const float hv = gt / (1.f + expf(-gt)) * up;   // SiLU(gate) * up
               const int col = (wn * (FN / 2) + fn) * 32 + lc;
-              *(uint16_t*)(stage + lds_off(row, col)) = f32_to_bf16(hv);
+              *(uint16_t*)(stage + lds_off(row, col)) =
+                  f32_to_bf16(silu_mul(acc[fm][fn][r], acc[fm][fn + FN / 2][r]));
             }
           } else {
+            const float g = s_gate[row];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-              const int col = fn * 32 + lc;
-              *(uint16_t*)(stage + lds_off(row, col)) = f32_to_bf16(acc[fm][fn][r] * g);
-            }
+            for (int fn = 0; fn < FN; ++fn)
+              *(uint16_t*)(stage + lds_off(row, fn * 32 + lc)) = f32_to_bf16(acc[fm][fn][r] * g);
           }
         }
       }
     }
-    __syncthreads();
-    // ---- LDS -> global, 16 bytes per thread per chunk
-    for (int i = threadIdx.x; i < BM * CPRW; i += NTHREADS) {
+    lds_sync();
+    for (int i = threadIdx.x; i < kPipeBM * CPRW; i += kPipeThreads) {
       const int row = i / CPRW, c = i % CPRW;
-      const int p = ti.m0 + row;
-      if (p >= ti.rows) continue;
+      const int drow = s_dst[row];
+      if (drow < 0) continue;
       const u32x4 v = *(const u32x4*)(stage + row * (COLS * 2) + ((c ^ (row & 7)) << 4));
       uint16_t* dst;
-      if (MODE == 1) {
-        dst = ti.routed ? (uint16_t*)a.H_routed + (size_t)(ti.row_base + p) * a.I
-                        : (uint16_t*)a.H_shared + (size_t)p * a.K_s * a.I + (size_t)(ti.v - a.N) * a.I;
-        dst += ti.n0 + c * 8;
-      } else {
-        if (ti.routed) {
-          int pair = a.sorted_pair[ti.row_base + p];
-          pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
-          dst = (uint16_t*)a.Y + (size_t)pair * a.d;
-        } else {
-          dst = (uint16_t*)a.Y_shared + (size_t)p * a.d;
-        }
-        dst += ti.n0 + pass * COLS + c * 8;
-      }
+      if (MODE == 1)
+        dst = ti.routed ? (uint16_t*)a.H_routed + (size_t)drow * a.I + ti.n0 + c * 8
+                        : (uint16_t*)a.H_shared + (size_t)drow * a.K_s * a.I +
+                              (size_t)(ti.v - a.N) * a.I + ti.n0 + c * 8;
+      else
+        dst = (ti.routed ? (uint16_t*)a.Y : (uint16_t*)a.Y_shared) + (size_t)drow * a.d + ti.n0 +
+              pass * COLS + c * 8;
       *(u32x4*)dst = v;
     }
-    __syncthreads();
+    lds_sync();
   }
 }
 
-template <class E, int WM, int RB, int STAGES, int MINB, int MODE>
-__global__ __launch_bounds__(WM * 128, MINB) void expert_gemm_dma_kernel(ExpertArgs a) {
+// Destination row (and gate) of tile row r: H slot / pair index / token, or -1.
+template <int MODE>
+__device__ __forceinline__ void pipe_row_dest(const ExpertArgs& a, const Tile& ti, int r, int& dst,
+                                              float& g) {
+  const int p = ti.m0 + r;
+  g = 1.f;
+  dst = -1;
+  if (p >= ti.rows) return;
+  if (MODE == 1 || !ti.routed) {
+    dst = (MODE == 1 && ti.routed) ? ti.row_base + p : p;
+    return;
+  }
+  const int TK = a.T * a.K;
+  int pair = a.sorted_pair[ti.row_base + p];
+  pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
+  dst = pair;
+  g = a.gate[pair];
+}
+
+template <class E, int MODE>
+__global__ __launch_bounds__(kPipeThreads, 1) void expert_gemm_pipe_kernel(ExpertArgs a) {
   using Tp = typename E::T;
-  constexpr int WN = 2, NWAVES = WM * WN;
-  constexpr int FM = 2, FN = 4;                // each wavefront: 64 rows x 128 columns
-  constexpr int BM = WM * FM * 32;
-  constexpr int BNB = 256;
-  constexpr int BNO = MODE == 1 ? BNB / 2 : BNB;
-  constexpr int ROWS = BM + BNB;
-  constexpr int CPR = RB / 16;                 // 16-byte chunks per row and k-step
-  constexpr int RPI = 64 / CPR;                // rows one wavefront load covers
-  constexpr int STAGE_BYTES = ROWS * RB;
-  constexpr int NINST = ROWS / (NWAVES * RPI); // loads per wavefront per stage
-  constexpr int kStep = RB / (int)sizeof(Tp);  // contraction elements per k-step
-  constexpr int KG = RB / 32;                  // 16-k groups per k-step (2 chunks each)
-  static_assert(RB == 64 || RB == 128, "row bytes");
-  static_assert(STAGES >= 2 && STAGES * STAGE_BYTES * MINB <= 152 * 1024, "LDS budget");
-  static_assert((STAGES - 2) * NINST <= 63, "vmcnt range");
-  // One array per ring slot, always addressed through a compile-time slot
-  // number: the compiler then knows that the direct-to-LDS loads filling one
-  // slot never alias the reads of another and does not wait for them.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGES > 2 ? STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds3[STAGES > 3 ? STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds4[STAGES > 4 ? STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds5[STAGES > 5 ? STAGE_BYTES : 16];
-  static_assert(STAGES <= 6, "ring slots");
+  constexpr int BNO = MODE == 1 ? kPipeBNB / 2 : kPipeBNB;
+  constexpr int kStep = kPipeRB / (int)sizeof(Tp);
+  constexpr int NINST = kPipeNinst;
+  constexpr bool kStaged = std::is_same<E, ElemBF16>::value;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kPipeSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kPipeSlot];
   __shared__ int s_tab[kMaxV + 1];
+  __shared__ int s_dst[kPipeBM];
+  __shared__ float s_gate[kPipeBM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  auto slot = [&](auto U) -> uint8_t* {
-    constexpr int u = decltype(U)::value;
-    if constexpr (u == 0) return lds0;
-    else if constexpr (u == 1) return lds1;
-    else if constexpr (u == 2) return lds2;
-    else if constexpr (u == 3) return lds3;
-    else if constexpr (u == 4) return lds4;
-    else return lds5;
-  };
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_a = min(max(kPipeBM / 8 - wave * NINST, 0), NINST);  // this wavefront's A-row loads
 
   // Persistent: the blocks of XCD x (blockIdx % 8, workgroups are dealt
-  // round-robin over the XCDs) walk that XCD's contiguous range of tiles in
-  // rounds, so the tiles of one round share an expert's weights and tokens in
-  // the XCD's L2 and move through the contraction together.
+  // round-robin over the XCDs) walk that XCD's contiguous range of tiles, so
+  // concurrent tiles share an expert's weights and tokens in the XCD's L2.
   const int V = load_tile_table<MODE>(a, s_tab);
   const int total = s_tab[V] * ((MODE == 1 ? a.I : a.d) / BNO);
-  const int X = min(8, (int)gridDim.x);  // groups (XCDs) that have blocks
+  const int X = min(8, (int)gridDim.x);
   const int x = blockIdx.x % X, lb = blockIdx.x / X;
   const int nbx = ((int)gridDim.x - x + X - 1) / X;
   const int q = total / X, rem = total % X;
   const int start = x * q + min(x, rem), end = start + q + (x < rem ? 1 : 0);
-  for (int L = start + lb; L < end; L += nbx) {
-  const Tile ti = tile_of<BM, BNO, MODE>(a, s_tab, V, L);
-  const int Kc = MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I);
-  const int nsteps = Kc / kStep;
-  const bool wave_active = ti.m0 + wm * FM * 32 < ti.rows;
-  // the previous tile's stores have left and every wavefront is done with the ring
-  MOE_WAIT_VMCNT(0);
-  MOE_WAIT_LGKMCNT0();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  int L = start + lb;
+  if (L >= end) return;
 
-  // Row groups q = wave*NINST + i (RPI rows each); lane -> row q*RPI + lane/CPR,
-  // slot lane%CPR, which holds chunk slot ^ swizzle(row).  Each lane keeps a
-  // 32-bit byte offset from the A operand's base (u or H) or the B operand's
-  // base (the expert's weight block); the bases are wavefront-uniform.
-  const uint8_t* a0 = (const uint8_t*)tile_row_ptr<E, MODE, BM, BNB>(a, ti, BM) ;  // B row 0
-  const uint8_t* a_base = MODE == 1 ? (const uint8_t*)a.u
-                                    : (const uint8_t*)(ti.routed ? a.H_routed : a.H_shared);
-  uint32_t off[NINST];
-#pragma unroll
-  for (int i = 0; i < NINST; ++i) {
-    const int r = (wave * NINST + i) * RPI + lane / CPR;
-    const uint8_t* rp = (const uint8_t*)tile_row_ptr<E, MODE, BM, BNB>(a, ti, r);
-    const int slot = lane % CPR;
-    const int chunk = RB == 128 ? (slot ^ ((r >> 1) & 7)) : (slot ^ ((r >> 2) & 3));
-    off[i] = (uint32_t)(rp - (r < BM ? a_base : a0)) + chunk * 16;
-  }
-  const int n_a = min(max(BM / RPI - wave * NINST, 0), NINST);  // this wavefront's A-row loads
-  auto bases = [&](int s, const uint8_t*& ab, const uint8_t*& bb) {
-    const size_t k0 = (size_t)s * kStep;
-    ab = a_base + k0 * sizeof(Tp);
-    bb = a0 + b_offset<MODE>(a, ti, k0) * sizeof(Tp);
-  };
-  auto issue = [&](auto U, int s) {  // k-step s into ring slot U
-    const uint8_t *ab, *bb;
-    bases(s, ab, bb);
-    dma_fill<NINST>(slot(U) + wave * NINST * 1024, ab, bb, off, n_a);
-  };
+  Tile ti = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, L));
+  PipeLoads ld;
+  pipe_prepare<E, MODE>(a, ti, wave, lane, ld);
+  pipe_issue<E, MODE>(a, ti, ld, 0, n_a, lds0 + wave * NINST * 1024);
 
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  while (true) {
+    const int Kc = MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I);
+    const int nsteps = Kc / kStep;  // even (the host only picks this kernel then)
+    const bool active = ti.m0 + wm * 64 < ti.rows;
+    const int Ln = L + nbx;
+    const bool has_next = Ln < end;
+    // destination row and gate of tile row `tid`, kept in registers until the epilogue
+    int my_dst = -1;
+    float my_gate = 1.f;
+    if (tid < kPipeBM) pipe_row_dest<MODE>(a, ti, tid, my_dst, my_gate);
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
-  using I5 = std::integral_constant<int, 5>;
-  // prologue: k-steps 0 .. STAGES-2 into slots 0 .. STAGES-2.  Loads are
-  // issued unconditionally (k-steps past the end repeat the last one into a
-  // slot nobody reads), so every step waits for the same count.
-  const int last = nsteps - 1;
-  issue(I0{}, 0);
-  if constexpr (STAGES > 2) issue(I1{}, min(1, last));
-  if constexpr (STAGES > 3) issue(I2{}, min(2, last));
-  if constexpr (STAGES > 4) issue(I3{}, min(3, last));
-  if constexpr (STAGES > 5) issue(I4{}, min(4, last));
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // k-step s reads slot s % STAGES and refills slot (s - 1) % STAGES with k-step s + STAGES - 1
-  auto step = [&](auto U, int s) {
-    constexpr int u = decltype(U)::value;
-    using W = std::integral_constant<int, (u + STAGES - 1) % STAGES>;
-    // stage s has landed once only the STAGES-2 later stages are in flight
-    MOE_WAIT_VMCNT((STAGES - 2) * NINST);
-    MOE_WAIT_LGKMCNT0();  // this wavefront's reads of the slot about to be refilled are done
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    const uint8_t *ab, *bb;
-    bases(min(s + STAGES - 1, last), ab, bb);
-    dma_kstep<E, NINST, KG, FM, FN, RB, BM, BNB, MODE>(slot(U), slot(W{}) + wave * NINST * 1024,
-                                                       ab, bb, off, n_a, wave_active, wm, wn,
-                                                       lane, acc);
-  };
-  for (int s0 = 0; s0 < nsteps; s0 += STAGES) {
-    step(I0{}, s0);
-    if (s0 + 1 < nsteps) step(I1{}, s0 + 1);
-    if constexpr (STAGES > 2) if (s0 + 2 < nsteps) step(I2{}, s0 + 2);
-    if constexpr (STAGES > 3) if (s0 + 3 < nsteps) step(I3{}, s0 + 3);
-    if constexpr (STAGES > 4) if (s0 + 4 < nsteps) step(I4{}, s0 + 4);
-    if constexpr (STAGES > 5) if (s0 + 5 < nsteps) step(I5{}, s0 + 5);
-  }
-  if constexpr (std::is_same<E, ElemBF16>::value && STAGE_BYTES >= BM * 256) {
-    // the ring is free once every wavefront has finished its last reads
-    MOE_WAIT_VMCNT(0);
-    MOE_WAIT_LGKMCNT0();
-    __syncthreads();
-    store_tile_bf16_lds<MODE, FM, FN, BM, WM * 128>(a, ti, wm, wn, acc, lds0);
-  } else {
-    store_tile<E, MODE, FM, FN>(a, ti, wm, wn, acc);
-  }
+    Tile tn = ti;
+    PipeLoads ldn = ld;
+    for (int s = 0; s < nsteps; s += 2) {
+      // even k-step: slot 0 holds k-step s; k-step s + 1 goes to slot 1
+      pipe_sync();
+      pipe_issue<E, MODE>(a, ti, ld, s + 1, n_a, lds1 + wave * NINST * 1024);
+      if (active) pipe_mma<E, MODE>(lds0, wm, wn, lane, acc);
+      // odd k-step: slot 1 holds k-step s + 1; slot 0 gets k-step s + 2, or
+      // the next tile's first k-step after the last one
+      if (s + 2 >= nsteps && has_next) {
+        tn = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, Ln));
+        pipe_prepare<E, MODE>(a, tn, wave, lane, ldn);
+      }
+      pipe_sync();
+      if (s + 2 < nsteps)
+        pipe_issue<E, MODE>(a, ti, ld, s + 2, n_a, lds0 + wave * NINST * 1024);
+      else if (has_next)
+        pipe_issue<E, MODE>(a, tn, ldn, 0, n_a, lds0 + wave * NINST * 1024);
+      if (active) pipe_mma<E, MODE>(lds1, wm, wn, lane, acc);
+    }
+
+    // epilogue: slot 1 is free once every wavefront has finished its last reads
+    if (tid < kPipeBM) {
+      s_dst[tid] = my_dst;
+      s_gate[tid] = my_gate;
+    }
+    lds_sync();
+    if constexpr (kStaged) {
+      pipe_store_bf16<MODE>(a, ti, wm, wn, acc, lds1, s_dst, s_gate);
+    } else {
+      store_tile<E, MODE, 2, 4>(a, ti, wm, wn, acc);
+      __syncthreads();
+    }
+    if (!has_next) break;
+    L = Ln;
+    ti = tn;
+    ld = ldn;
   }
 }
 
-// Kernel variants.  kind 0: register-staged kernel with wavefronts WM x WN and
-// 32x32 fragments FM x FN per wavefront.  kind 1: LDS-DMA kernel with
-// BM x 256 tiles (FM = BM / 64), rb bytes per row per k-step, `stages` LDS
-// buffers and minb blocks per CU.
+// Kernel choice.  kind 0: register-staged kernel with wavefronts WM x WN and
+// 32x32 fragments FM x FN per wavefront; kind 1: the pipelined LDS-DMA kernel.
 struct Shape {
-  int kind, WM, WN, FM, FN, stages, rb, minb;
-  int bm() const { return kind == 1 ? FM * 64 : WM * FM * 32; }
+  int kind, WM, WN, FM, FN;
+  int bm() const { return kind == 1 ? kPipeBM : WM * FM * 32; }
 };
 
 // Few tokens per expert (decode-sized batches): short M tiles, wide N tiles,
 // so every CU streams a large weight slab.
 bool small_m(const ExpertArgs& a) { return (long long)a.T * a.K < 64LL * a.N; }
 
-// Tuning override, read once:
-// MOE_GEMM_VARIANT = reg | dma128 | dma256k32 | dma128k32 | dma128k32x6 | dma256
-int variant_override() {
+// MOE_GEMM_VARIANT=reg forces the register-staged kernel (read once; for tuning runs).
+bool force_reg() {
   static int v = [] {
     const char* e = getenv("MOE_GEMM_VARIANT");
-    if (e == nullptr) return -1;
-    const char* names[] = {"reg", "dma128", "dma256k32", "dma128k32", "dma128k32x6", "dma256"};
-    for (int i = 0; i < 6; ++i)
-      if (!strcmp(e, names[i])) return i;
-    return -1;
+    return (e != nullptr && !strcmp(e, "reg")) ? 1 : 0;
   }();
-  return v;
+  return v != 0;
 }
 
-constexpr int kDefaultVariant = 5;
+// The pipelined kernel needs 128-column H tiles (I % 128), 256-column Y tiles
+// (d % 256) and an even number of 128-byte k-steps in every contraction.
+bool pipe_ok1(const ExpertArgs& a, int es) { return a.I % 128 == 0 && (a.d * es) % 256 == 0; }
+bool pipe_ok2(const ExpertArgs& a, int es) { return a.d % 256 == 0 && (a.I * es) % 256 == 0; }
 
-Shape dma_shape(int variant) {
-  switch (variant) {
-    case 2: return Shape{1, 4, 2, 4, 4, 4, 64, 1};    // 256 x 256, 8 wavefronts, 4 x 32 KB
-    case 3: return Shape{1, 2, 2, 2, 4, 3, 64, 2};    // 128 x 256, 3 x 24 KB, 2 blocks/CU
-    case 4: return Shape{1, 2, 2, 2, 4, 6, 64, 1};    // 128 x 256, 6 x 24 KB
-    case 5: return Shape{1, 4, 2, 4, 4, 2, 128, 1};   // 256 x 256, 8 wavefronts, 2 x 64 KB
-    default: return Shape{1, 2, 2, 2, 4, 3, 128, 1};  // 128 x 256, 3 x 48 KB
-  }
+Shape shape1(const ExpertArgs& a, int es) {
+  if (small_m(a)) return a.I % 128 == 0 ? Shape{0, 1, 4, 1, 2} : Shape{0, 2, 2, 1, 2};
+  if (!force_reg() && pipe_ok1(a, es)) return Shape{1, 4, 2, 2, 4};
+  return Shape{0, 2, 2, 2, 2};
 }
-
-Shape shape1(const ExpertArgs& a) {
-  if (small_m(a)) return a.I % 128 == 0 ? Shape{0, 1, 4, 1, 2, 2, 128, 2} : Shape{0, 2, 2, 1, 2, 2, 128, 2};
-  const int ov = variant_override();
-  if (a.I % 128 == 0 && ov != 0) return dma_shape(ov < 0 ? kDefaultVariant : ov);
-  return Shape{0, 2, 2, 2, 2, 2, 128, 2};
-}
-Shape shape2(const ExpertArgs& a) {
-  if (small_m(a)) return a.d % 256 == 0 ? Shape{0, 1, 4, 1, 2, 2, 128, 2} : Shape{0, 2, 2, 1, 1, 2, 128, 2};
-  const int ov = variant_override();
-  if (a.d % 256 == 0 && ov != 0) return dma_shape(ov < 0 ? kDefaultVariant : ov);
-  return a.d % 128 == 0 ? Shape{0, 2, 2, 2, 2, 2, 128, 2} : Shape{0, 2, 2, 2, 1, 2, 128, 2};
+Shape shape2(const ExpertArgs& a, int es) {
+  if (small_m(a)) return a.d % 256 == 0 ? Shape{0, 1, 4, 1, 2} : Shape{0, 2, 2, 1, 1};
+  if (!force_reg() && pipe_ok2(a, es)) return Shape{1, 4, 2, 2, 4};
+  return a.d % 128 == 0 ? Shape{0, 2, 2, 2, 2} : Shape{0, 2, 2, 2, 1};
 }
 
 long long grid_tiles(const ExpertArgs& a, int bm, int nt, int mode) {
@@ -742,28 +746,21 @@ int cu_count() {
   return cache[dev];
 }
 
-template <class E, int WM, int RB, int STAGES, int MINB, int MODE>
-hipError_t launch_dma(const ExpertArgs& a, hipStream_t st) {
-  constexpr int BM = WM * 64;
-  constexpr int BNO = MODE == 1 ? 128 : 256;
-  long long g = grid_tiles(a, BM, (MODE == 1 ? a.I : a.d) / BNO, MODE);
+template <class E, int MODE>
+hipError_t launch_pipe(const ExpertArgs& a, hipStream_t st) {
+  constexpr int BNO = MODE == 1 ? kPipeBNB / 2 : kPipeBNB;
+  long long g = grid_tiles(a, kPipeBM, (MODE == 1 ? a.I : a.d) / BNO, MODE);
   if (g <= 0) return hipSuccess;
-  g = std::min<long long>(g, (long long)cu_count() * MINB);  // persistent: one block per slot
-  expert_gemm_dma_kernel<E, WM, RB, STAGES, MINB, MODE>
-      <<<dim3((unsigned)g), dim3(WM * 128), 0, st>>>(a);
+  g = std::min<long long>(g, (long long)cu_count());  // persistent: one block per CU
+  expert_gemm_pipe_kernel<E, MODE><<<dim3((unsigned)g), dim3(kPipeThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
 template <class E, int MODE>
 hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
-  const Shape s = MODE == 1 ? shape1(a) : shape2(a);
-  if (s.kind == 1) {
-    if (s.FM == 4 && s.rb == 128) return launch_dma<E, 4, 128, 2, 1, MODE>(a, st);
-    if (s.FM == 4) return launch_dma<E, 4, 64, 4, 1, MODE>(a, st);
-    if (s.rb == 64 && s.minb == 2) return launch_dma<E, 2, 64, 3, 2, MODE>(a, st);
-    if (s.rb == 64) return launch_dma<E, 2, 64, 6, 1, MODE>(a, st);
-    return launch_dma<E, 2, 128, 3, 1, MODE>(a, st);
-  }
+  const int es = (int)sizeof(typename E::T);
+  const Shape s = MODE == 1 ? shape1(a, es) : shape2(a, es);
+  if (s.kind == 1) return launch_pipe<E, MODE>(a, st);
   if (MODE == 1) {
     if (s.WM == 1) return launch_reg<E, 1, 4, 1, 2, 1>(a, st);
     if (s.FM == 1) return launch_reg<E, 2, 2, 1, 2, 1>(a, st);
@@ -780,9 +777,10 @@ hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
 int expert_tile_table_ints(int N, int K_s) { return (N + K_s + 1) + (N + 2); }
 
 hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream) {
-  (void)dtype;
-  tile_table_kernel<<<1, 64, 0, stream>>>(a.offsets, a.N, a.K_s, a.T, a.T * a.K, shape1(a).bm(),
-                                          shape2(a).bm(), a.tiles1, a.tiles2);
+  const int es = dtype == 1 ? 2 : 4;
+  tile_table_kernel<<<1, 64, 0, stream>>>(a.offsets, a.N, a.K_s, a.T, a.T * a.K,
+                                          shape1(a, es).bm(), shape2(a, es).bm(), a.tiles1,
+                                          a.tiles2);
   return hipGetLastError();
 }
 
