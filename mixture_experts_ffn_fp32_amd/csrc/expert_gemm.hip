@@ -604,13 +604,22 @@ __global__ __launch_bounds__(kPipeThreads, 1) void expert_gemm_pipe_kernel(Exper
   // Persistent: the blocks of XCD x (blockIdx % 8, workgroups are dealt
   // round-robin over the XCDs) walk that XCD's contiguous range of tiles, so
   // concurrent tiles share an expert's weights and tokens in the XCD's L2.
+  // The ranges split the work, not the tile count: a GEMM2 tile of the shared
+  // experts contracts over K_s * I and costs K_s routed tiles.
   const int V = load_tile_table<MODE>(a, s_tab);
-  const int total = s_tab[V] * ((MODE == 1 ? a.I : a.d) / BNO);
+  const int nt = (MODE == 1 ? a.I : a.d) / BNO;
+  const int total = s_tab[V] * nt;
+  const int Lr = MODE == 2 ? s_tab[a.N] * nt : total;  // tiles before the shared ones
+  const int w = MODE == 2 ? max(a.K_s, 1) : 1;
+  const long long Wt = Lr + (long long)(total - Lr) * w;
   const int X = min(8, (int)gridDim.x);
   const int x = blockIdx.x % X, lb = blockIdx.x / X;
   const int nbx = ((int)gridDim.x - x + X - 1) / X;
-  const int q = total / X, rem = total % X;
-  const int start = x * q + min(x, rem), end = start + q + (x < rem ? 1 : 0);
+  // first tile whose cumulative cost reaches c
+  auto first_at = [&](long long c) -> int {
+    return c <= Lr ? (int)c : Lr + (int)((c - Lr + w - 1) / w);
+  };
+  const int start = first_at(Wt * x / X), end = first_at(Wt * (x + 1) / X);
   int L = start + lb;
   if (L >= end) return;
 
