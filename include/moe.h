@@ -130,6 +130,31 @@ moe_status_t moe_expert_ffn(const void* u, const void* W_routed, const void* W_s
 moe_status_t moe_combine(const void* u, const void* Y, const void* Y_shared, int T, int d,
                          int K, int K_s, int dtype, void* h, void* stream);
 
+/* ---- balance statistics (beside the forward path) ----
+ * DeepSeekMoE paper summary, papercache.org, sec. 3.3 (expert-level and
+ * device-level balance losses), over one batch of T >= 1 tokens:
+ *   f_i = N / (K T) * #{t : token t selects routed expert i}
+ *   P_i = (1/T) * sum_t s_{i,t}
+ *   L_ExpBal = alpha1 * sum_i f_i P_i
+ *   f'_g = mean of f_i over the experts of device group g
+ *   P'_g = sum of P_i over the experts of device group g
+ *   L_DevBal = alpha2 * sum_g f'_g P'_g
+ * (N, K are the paper's N' = mN - K_s and K' = mK - K_s.)
+ * Inputs: scores [T][N] float32 (the softmax s from moe_route), idx [T][K]
+ * int32 (entries outside [0, N) are not counted).
+ * group_of is a HOST array of N ints giving each routed expert's group in
+ * [0, D), every group non-empty; or NULL (then D is ignored, f_dev / P_dev may
+ * be NULL and L_DevBal is written as 0).
+ * Outputs (device, float32): f [N], P [N], f_dev [D], P_dev [D],
+ * losses [2] = {L_ExpBal, L_DevBal}.  Sums are formed in float64 in a fixed
+ * order, so repeated calls give identical bits.
+ * Workspace: moe_balance_workspace_size() bytes (partial sums). */
+moe_status_t moe_balance_workspace_size(int T, int N, size_t* bytes);
+moe_status_t moe_balance_stats(const float* scores, const int32_t* idx, int T, int N, int K,
+                               const int32_t* group_of, int D, float alpha1, float alpha2,
+                               float* f, float* P, float* f_dev, float* P_dev, float* losses,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- per-stage timing (for profiling; off by default) ----
  * When enabled, moe_layer_forward records a HIP event pair around each of its
  * kernel stages on the stream it was given.  moe_timing_read() waits for

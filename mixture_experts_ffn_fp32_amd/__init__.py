@@ -3,5 +3,5 @@
 The library (libmoe.so, built by ``python -m mixture_experts_ffn_fp32_amd.build``)
 does all of the layer's work; this package only marshals arguments to it.
 """
-from .moe import (MoEError, STAGE_NAMES, combine, dispatch, expert_ffn, layer_forward,  # noqa: F401
+from .moe import (MoEError, STAGE_NAMES, balance_stats, combine, dispatch, expert_ffn, layer_forward,  # noqa: F401
                   load_library, route, timing_enable, timing_read, workspace_size)

@@ -411,6 +411,53 @@ moe_status_t moe_combine(const void* u, const void* Y, const void* Y_shared, int
   return ok();
 }
 
+moe_status_t moe_balance_workspace_size(int T, int N, size_t* bytes) {
+  if (T < 1) return fail(MOE_ERR_INVALID_ARG, "balance statistics need T >= 1");
+  if (N < 1) return fail(MOE_ERR_INVALID_ARG, "N must be >= 1");
+  if (N > 256) return fail(MOE_ERR_UNSUPPORTED, "N > 256 routed experts is not supported");
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = moe::balance_workspace_bytes(T, N);
+  return ok();
+}
+
+moe_status_t moe_balance_stats(const float* scores, const int32_t* idx, int T, int N, int K,
+                               const int32_t* group_of, int D, float alpha1, float alpha2,
+                               float* f, float* P, float* f_dev, float* P_dev, float* losses,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t s = check_routing(T, N, K);
+  if (s != MOE_OK) return s;
+  if (T < 1) return fail(MOE_ERR_INVALID_ARG, "balance statistics need T >= 1");
+  moe::BalanceGroups groups{};
+  if (group_of != nullptr) {
+    if (D < 1 || D > N) return fail(MOE_ERR_INVALID_ARG, "D must satisfy 1 <= D <= N");
+    std::vector<int> size(D, 0);
+    for (int i = 0; i < N; ++i) {
+      if (group_of[i] < 0 || group_of[i] >= D)
+        return fail(MOE_ERR_INVALID_ARG, "group_of[" + std::to_string(i) + "] is outside [0, D)");
+      ++size[group_of[i]];
+      groups.of[i] = group_of[i];
+    }
+    for (int g = 0; g < D; ++g)
+      if (size[g] == 0)
+        return fail(MOE_ERR_INVALID_ARG, "device group " + std::to_string(g) + " has no expert");
+    groups.D = D;
+  }
+  if ((s = check_ptr("scores", scores, true)) != MOE_OK) return s;
+  if ((s = check_ptr("idx", idx, true)) != MOE_OK) return s;
+  if ((s = check_ptr("f", f, true)) != MOE_OK) return s;
+  if ((s = check_ptr("P", P, true)) != MOE_OK) return s;
+  if ((s = check_ptr("f_dev", f_dev, group_of != nullptr)) != MOE_OK) return s;
+  if ((s = check_ptr("P_dev", P_dev, group_of != nullptr)) != MOE_OK) return s;
+  if ((s = check_ptr("losses", losses, true)) != MOE_OK) return s;
+  if ((s = check_ptr("workspace", workspace, true)) != MOE_OK) return s;
+  if (workspace_bytes < moe::balance_workspace_bytes(T, N))
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_balance_workspace_size()");
+  hipError_t e = moe::launch_balance(scores, idx, T, N, K, groups, alpha1, alpha2, f, P, f_dev,
+                                     P_dev, losses, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "balance statistics launch");
+  return ok();
+}
+
 moe_status_t moe_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_timing.mu);
   g_timing.on = on != 0;

@@ -103,6 +103,19 @@ hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream)
 hipError_t launch_gemm1(int dtype, const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_gemm2(int dtype, const ExpertArgs& a, hipStream_t stream);
 
+// Balance statistics: per-chunk partial sums, then one block.  groups.of[i]
+// is the device group of routed expert i (D = 0: no device groups).
+constexpr int kBalRows = 128;
+struct BalanceGroups {
+  int D;
+  int32_t of[256];
+};
+size_t balance_workspace_bytes(int T, int N);
+hipError_t launch_balance(const float* scores, const int32_t* idx, int T, int N, int K,
+                          const BalanceGroups& groups, float alpha1, float alpha2, float* f,
+                          float* P, float* f_dev, float* P_dev, float* losses, void* workspace,
+                          hipStream_t stream);
+
 hipError_t launch_combine(int dtype, const void* u, const void* Y, const void* Y_shared, int T,
                           int d, int K, int K_s, void* h, hipStream_t stream);
 

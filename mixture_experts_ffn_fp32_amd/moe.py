@@ -22,7 +22,8 @@ _DTYPES = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}
 
 EXPORTED = ("moe_last_error", "moe_workspace_size", "moe_layer_forward", "moe_route",
             "moe_dispatch_workspace_size", "moe_dispatch", "moe_expert_ffn_workspace_size",
-            "moe_expert_ffn", "moe_combine", "moe_timing_enable", "moe_timing_read")
+            "moe_expert_ffn", "moe_combine", "moe_balance_workspace_size", "moe_balance_stats",
+            "moe_timing_enable", "moe_timing_read")
 
 
 class MoEError(RuntimeError):
@@ -56,6 +57,9 @@ def load_library(path: str = LIB_PATH):
         "moe_expert_ffn_workspace_size": [i, i, i, i, szp],
         "moe_expert_ffn": [vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [vp, vp, vp, i, i, i, i, i, vp, vp],
+        "moe_balance_workspace_size": [i, i, szp],
+        "moe_balance_stats": [vp, vp, i, i, i, vp, i, ctypes.c_float, ctypes.c_float, vp, vp, vp,
+                              vp, vp, vp, sz, vp],
         "moe_timing_enable": [i],
         "moe_timing_read": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)],
     }
@@ -195,6 +199,41 @@ def combine(u, Y, Y_shared, K: int, K_s: int):
     _check(L.moe_combine(_p(u), _p(Y), _p(Y_shared), T, d, K, K_s, _dtype_code(u), _p(h),
                          _stream()))
     return h
+
+
+def balance_stats(scores, idx, K: int, group_of=None, alpha1: float = 1.0, alpha2: float = 1.0):
+    """Balance statistics of one batch: dict of f [N], P [N], L_ExpBal and, with
+    group_of (a length-N sequence of device-group ids 0..D-1), f_dev [D],
+    P_dev [D], L_DevBal.  Tensors are float32 on the scores' device."""
+    L = load_library()
+    T, N = scores.shape
+    _dev(scores, dtype=torch.float32)
+    _dev(idx, dtype=torch.int32)
+    if idx.shape != (T, K):
+        raise MoEError(1, "idx must be [T][K]")
+    D = 0
+    groups = None
+    if group_of is not None:
+        g = [int(x) for x in group_of]
+        if len(g) != N:
+            raise MoEError(1, "group_of must have N entries")
+        D = max(g) + 1 if g else 0
+        groups = (ctypes.c_int32 * N)(*g)
+    out = ctypes.c_size_t(0)
+    _check(L.moe_balance_workspace_size(T, N, ctypes.byref(out)))
+    dev = scores.device
+    ws = torch.empty(max(out.value, 1), dtype=torch.uint8, device=dev)
+    f = torch.empty(N, dtype=torch.float32, device=dev)
+    P = torch.empty(N, dtype=torch.float32, device=dev)
+    fd = torch.empty(max(D, 1), dtype=torch.float32, device=dev)
+    Pd = torch.empty(max(D, 1), dtype=torch.float32, device=dev)
+    losses = torch.empty(2, dtype=torch.float32, device=dev)
+    _check(L.moe_balance_stats(_p(scores), _p(idx), T, N, K, groups, D, alpha1, alpha2, _p(f),
+                               _p(P), _p(fd), _p(Pd), _p(losses), _p(ws), ws.numel(), _stream()))
+    res = {"f": f, "P": P, "L_ExpBal": losses[0]}
+    if group_of is not None:
+        res.update({"f_dev": fd[:D], "P_dev": Pd[:D], "L_DevBal": losses[1]})
+    return res
 
 
 def timing_enable(on: bool = True):

@@ -118,3 +118,29 @@ def test_binding_refuses_host_tensors():
     u = torch.zeros(4, 64)
     with pytest.raises(mx.MoEError):
         mx.layer_forward(u, torch.zeros(8, 64), torch.zeros(8 * 3 * 64 * 64), None, 8, 2, 0)
+
+
+def _bal(lib, scores=16, idx=32, T=8, N=8, K=2, group_of=None, D=0, f=64, P=96, fd=128, Pd=160,
+         losses=192, ws=4096, wsb=1 << 30):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)   # noqa: E731
+    g = None if group_of is None else (ctypes.c_int32 * len(group_of))(*group_of)
+    return lib.moe_balance_stats(p(scores), p(idx), T, N, K, g, D, 1.0, 1.0, p(f), p(P), p(fd),
+                                 p(Pd), p(losses), p(ws), wsb, None)
+
+
+def test_balance_validation_never_reaches_the_gpu(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.moe_balance_workspace_size(8, 8, ctypes.byref(out)) == OK and out.value > 0
+    assert lib.moe_balance_workspace_size(0, 8, ctypes.byref(out)) == INVALID
+    assert lib.moe_balance_workspace_size(8, 257, ctypes.byref(out)) == UNSUPPORTED
+    assert _bal(lib, T=0) == INVALID                       # the statistics divide by T
+    assert _bal(lib, K=9) == INVALID
+    assert _bal(lib, scores=None) == INVALID
+    assert _bal(lib, f=8) == ALIGNMENT
+    assert _bal(lib, wsb=16) == WORKSPACE
+    assert _bal(lib, group_of=[0, 0, 1, 1, 2, 2, 3, 3], D=4, fd=None) == INVALID
+    assert _bal(lib, group_of=[0, 0, 1, 1, 2, 2, 3, 4], D=4) == INVALID   # id outside [0, D)
+    assert "outside" in lib.moe_last_error().decode()
+    assert _bal(lib, group_of=[0, 0, 1, 1, 3, 3, 3, 3], D=4) == INVALID   # group 2 is empty
+    assert "no expert" in lib.moe_last_error().decode()
+    assert _bal(lib, group_of=[0] * 8, D=9) == INVALID

@@ -173,3 +173,65 @@ def test_empty_batch():
     h = mx.layer_forward(up.u[:0], up.E, up.W_routed, up.W_shared, w.N, w.K, w.K_s)
     torch.cuda.synchronize()
     assert h.shape == (0, w.d)
+
+
+def _check_balance(res, ref, groups):
+    f, P = res["f"].cpu().numpy(), res["P"].cpu().numpy()
+    # f_i = N count_i / (K T): an exact rational rounded once to float32
+    np.testing.assert_allclose(f, ref["f"], rtol=2.0 ** -23, atol=0)
+    np.testing.assert_allclose(P, ref["P"], rtol=2.0 ** -22, atol=1e-30)
+    assert abs(float(res["L_ExpBal"]) - ref["L_ExpBal"]) <= 2.0 ** -22 * abs(ref["L_ExpBal"])
+    if groups is not None:
+        np.testing.assert_allclose(res["f_dev"].cpu().numpy(), ref["f_dev"], rtol=2.0 ** -22)
+        np.testing.assert_allclose(res["P_dev"].cpu().numpy(), ref["P_dev"], rtol=2.0 ** -22)
+        assert abs(float(res["L_DevBal"]) - ref["L_DevBal"]) <= 2.0 ** -22 * abs(ref["L_DevBal"])
+
+
+@pytest.mark.parametrize("grouping", ["none", "contiguous", "scattered"])
+def test_balance_statistics(small, grouping):
+    """Balance statistics of the GPU's own routing against the oracle's formulas on the
+    same scores and indices (float32 scores read exactly as float64)."""
+    w = small.w
+    idx, _, scores = mx.route(small.u, small.E, w.K, small.bias, want_scores=True)
+    D = min(4, w.N)
+    if grouping == "none":
+        group_of = None
+    elif grouping == "contiguous":
+        group_of = [i * D // w.N for i in range(w.N)]
+    else:
+        perm = np.random.default_rng(w.seed).permutation(w.N)
+        group_of = [int(perm[i]) % D for i in range(w.N)]
+    say(f"balance {w.name} {grouping}")
+    res = mx.balance_stats(scores, idx, w.K, group_of, alpha1=0.003, alpha2=0.05)
+    res2 = mx.balance_stats(scores, idx, w.K, group_of, alpha1=0.003, alpha2=0.05)
+    torch.cuda.synchronize()
+    groups = None if group_of is None else [[i for i in range(w.N) if group_of[i] == g]
+                                            for g in range(D)]
+    ref = oracle.balance_statistics(scores.cpu().numpy().astype(np.float64), idx.cpu().numpy(),
+                                    w.K, groups, alpha1=0.003, alpha2=0.05)
+    _check_balance(res, ref, groups)
+    for k in res:   # fixed summation order: identical bits on a second call
+        assert torch.equal(res[k], res2[k]), k
+    # the sums the definitions fix: sum_i f_i = N, sum_i P_i = 1
+    assert abs(float(res["f"].double().sum()) - w.N) <= 1e-5 * w.N
+    assert abs(float(res["P"].double().sum()) - 1.0) <= 1e-5
+
+
+def test_balance_statistics_ignores_out_of_range_indices():
+    T, N, K = 257, 12, 3
+    rng = np.random.default_rng(7)
+    s = rng.random((T, N))
+    s /= s.sum(axis=1, keepdims=True)
+    idx = np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)
+    bad = idx.copy()
+    bad[::5, 0] = -1
+    bad[1::7, 1] = N
+    say("balance out-of-range indices")
+    res = mx.balance_stats(torch.from_numpy(s.astype(np.float32)).cuda(),
+                           torch.from_numpy(bad).cuda(), K)
+    torch.cuda.synchronize()
+    keep = (bad >= 0) & (bad < N)
+    counts = np.bincount(bad[keep], minlength=N)
+    np.testing.assert_allclose(res["f"].cpu().numpy(), N / (K * T) * counts, rtol=2.0 ** -23)
+    np.testing.assert_allclose(res["P"].cpu().numpy(),
+                               s.astype(np.float32).astype(np.float64).sum(0) / T, rtol=2.0 ** -22)

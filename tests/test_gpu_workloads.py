@@ -145,3 +145,31 @@ def test_layer_forward_sampled(wl):
     rel = check_h(hs, h_ref, inp.u_f32()[tokens].astype(np.float64), tol_for(w), w.dtype, w.K,
                   w.name)
     say(f"{w.name}: max|dh|/max|h| = {rel:.2e} over {len(tokens)} tokens")
+
+
+def test_balance_statistics(wl):
+    """GPU statistics from the GPU's routing against the oracle's statistics from the
+    oracle's routing: P to float32 softmax accuracy, f to the tokens whose routing may
+    legitimately differ (near ties), and the definitions' exact sums."""
+    up, s = wl
+    w = up.w
+    D = 8 if w.N % 8 == 0 else 7 if w.N % 7 == 0 else 4
+    group_of = [i * D // w.N for i in range(w.N)]
+    groups = [[i for i in range(w.N) if group_of[i] == g] for g in range(D)]
+    say(f"balance {w.name}")
+    idx, _, scores = mx.route(up.u, up.E, w.K, up.bias, want_scores=True)
+    res = mx.balance_stats(scores, idx, w.K, group_of, alpha1=0.001, alpha2=0.05)
+    torch.cuda.synchronize()
+    idx_ref, _, margin = oracle.top_k_gates(s, w.K)
+    ref = oracle.balance_statistics(s, idx_ref, w.K, groups, alpha1=0.001, alpha2=0.05)
+    n_near = int(np.count_nonzero(margin <= 1e-6))
+    f_step = w.N / (w.K * w.T)
+    assert np.abs(res["f"].cpu().numpy() - ref["f"]).max() <= f_step * n_near + 2.0 ** -23 * w.N
+    np.testing.assert_allclose(res["P"].cpu().numpy(), ref["P"], rtol=1e-5, atol=1e-7)
+    assert abs(float(res["L_ExpBal"]) - ref["L_ExpBal"]) <= 1e-4 * ref["L_ExpBal"] + 1e-3 * n_near
+    np.testing.assert_allclose(res["P_dev"].cpu().numpy(), ref["P_dev"], rtol=1e-5, atol=1e-7)
+    assert abs(float(res["f"].double().sum()) - w.N) <= 1e-5 * w.N
+    assert abs(float(res["P"].double().sum()) - 1.0) <= 1e-5
+    if w.zipf_s is not None:   # the skew shows: the hottest expert far above f = 1
+        assert ref["f"].max() > 5.0
+    say(f"{w.name}: max f = {ref['f'].max():.3f}, L_ExpBal/alpha1 = {ref['L_ExpBal'] / 0.001:.4f}")
