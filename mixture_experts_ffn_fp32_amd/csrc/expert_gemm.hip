@@ -358,17 +358,18 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
   __builtin_amdgcn_s_waitcnt(((n)&0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
 #define MOE_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14))
 
-// Direct-to-LDS loads of one k-step of this lane's rows into `wr`.  The
-// restrict qualifier gives the compiler an alias scope, so it never makes LDS
-// reads of the other ring slot wait for these loads (the kernel orders the
-// refill of a slot after its last reads with its own waits and barrier).
+// Direct-to-LDS loads of one k-step of this lane's rows into `wr` (every row
+// of a wavefront belongs to the same operand, so `base` is wavefront-uniform
+// and each load is a scalar base plus a 32-bit lane offset).  The restrict
+// qualifier gives the compiler an alias scope, so it never makes LDS reads of
+// the other ring slot wait for these loads (the kernel orders the refill of a
+// slot after its last reads with its own waits and barrier).
 template <int NINST>
-__device__ __forceinline__ void dma_fill(uint8_t* __restrict__ wr, const uint8_t* a_base,
-                                         const uint8_t* b_base, const uint32_t (&off)[NINST],
-                                         int n_a) {
+__device__ __forceinline__ void dma_fill(uint8_t* __restrict__ wr, const uint8_t* base,
+                                         const uint32_t (&off)[NINST]) {
 #pragma unroll
   for (int i = 0; i < NINST; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)((i < n_a ? a_base : b_base) + off[i]),
+    __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
                                      (__attribute__((address_space(3))) void*)(wr + i * 1024), 16,
                                      0, 0);
 }
@@ -388,8 +389,10 @@ __device__ __forceinline__ void load_frags(const uint8_t* __restrict__ rd, int k
 
 // ---------------------------------------------------------------- pipelined LDS-DMA kernel
 // Tiles of 256 rows x 256 B rows (GEMM1: 128 gate + 128 up rows of the same
-// columns; GEMM2: 256 output columns), eight wavefronts (4 x 2), each owning
-// 64 rows x 128 columns (2 x 4 fragments of 32 x 32).  Operands reach LDS by
+// columns; GEMM2: 256 output columns), W wavefronts in (W/2) x 2, each owning
+// 512/W rows x 128 columns (FM x 4 fragments of 32 x 32).  With W = 4 each
+// wavefront holds 256 float32 accumulators (in AGPRs) and every LDS fragment
+// feeds four MFMAs: a third less LDS read traffic than W = 8.  Operands reach LDS by
 // direct-to-LDS loads (global_load_lds_dwordx4: lane L of a wavefront writes
 // 16 bytes at the wavefront's LDS address + 16 L), one 128-byte k-step per
 // row, in a two-slot ring: k-step s + 1 lands while k-step s is multiplied.
@@ -397,15 +400,22 @@ __device__ __forceinline__ void load_frags(const uint8_t* __restrict__ rd, int k
 // belongs in LDS slot L).  The kernel is persistent; while a tile's results
 // are written out (staged through the free ring slot as bf16 rows), the next
 // tile's first k-step is already loading.  One block per CU.
-constexpr int kPipeBM = 256, kPipeBNB = 256, kPipeRB = 128, kPipeThreads = 512;
+constexpr int kPipeBM = 256, kPipeBNB = 256, kPipeRB = 128;
 constexpr int kPipeSlot = (kPipeBM + kPipeBNB) * kPipeRB;  // 64 KB
-constexpr int kPipeNinst = (kPipeBM + kPipeBNB) / (8 * 8);  // loads per wavefront per k-step
+template <int W>
+struct PipeCfg {
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kNinst = (kPipeBM + kPipeBNB) / (8 * W);  // loads per wavefront per k-step
+  static constexpr int FM = kPipeBM / (32 * (W / 2));            // row fragments per wavefront
+  static constexpr int FN = 4;
+};
 
 // Per-tile load state of one lane: operand bases and 32-bit byte offsets.
+template <int NI>
 struct PipeLoads {
-  const uint8_t* a_base;     // u (GEMM1) or H (GEMM2) at contraction index 0
-  const uint8_t* b_row0;     // the tile's first B row at contraction index 0
-  uint32_t off[kPipeNinst];  // this lane's chunk of each of its rows
+  const uint8_t* a_base;  // u (GEMM1) or H (GEMM2) at contraction index 0
+  const uint8_t* b_row0;  // the tile's first B row at contraction index 0
+  uint32_t off[NI];       // this lane's chunk of each of its rows
 };
 
 // Keeps a wavefront-uniform value in a scalar register.
@@ -427,39 +437,39 @@ __device__ __forceinline__ Tile uni(const Tile& t) {
   return u;
 }
 
-template <class E, int MODE>
+template <class E, int MODE, int NI>
 __device__ __forceinline__ void pipe_prepare(const ExpertArgs& a, const Tile& ti, int wave,
-                                             int lane, PipeLoads& ld) {
+                                             int lane, PipeLoads<NI>& ld) {
   ld.b_row0 = uni((const uint8_t*)tile_row_ptr<E, MODE, kPipeBM, kPipeBNB>(a, ti, kPipeBM));
   ld.a_base = uni(MODE == 1 ? (const uint8_t*)a.u
                             : (const uint8_t*)(ti.routed ? a.H_routed : a.H_shared));
 #pragma unroll
-  for (int i = 0; i < kPipeNinst; ++i) {
-    const int r = (wave * kPipeNinst + i) * 8 + (lane >> 3);
+  for (int i = 0; i < NI; ++i) {
+    const int r = (wave * NI + i) * 8 + (lane >> 3);
     const uint8_t* rp = (const uint8_t*)tile_row_ptr<E, MODE, kPipeBM, kPipeBNB>(a, ti, r);
     const int chunk = (lane & 7) ^ ((r >> 1) & 7);
     ld.off[i] = (uint32_t)(rp - (r < kPipeBM ? ld.a_base : ld.b_row0)) + chunk * 16;
   }
 }
 
-template <class E, int MODE>
+template <class E, int MODE, int NI>
 __device__ __forceinline__ void pipe_issue(const ExpertArgs& a, const Tile& ti,
-                                           const PipeLoads& ld, int s, int n_a,
+                                           const PipeLoads<NI>& ld, int s, bool is_a,
                                            uint8_t* __restrict__ wr) {
   using Tp = typename E::T;
   constexpr int kStep = kPipeRB / (int)sizeof(Tp);
   const size_t k0 = (size_t)s * kStep;
   const uint8_t* ab = ld.a_base + k0 * sizeof(Tp);
   const uint8_t* bb = ld.b_row0 + b_offset<MODE>(a, ti, k0) * sizeof(Tp);
-  dma_fill<kPipeNinst>(wr, ab, bb, ld.off, n_a);
+  dma_fill<NI>(wr, uni(is_a ? ab : bb), ld.off);
 }
 
 // Multiplies one k-step out of slot `rd` (fragments of the next 16-k group are
 // read while the current one is on the MFMA pipe).
-template <class E, int MODE>
+template <class E, int MODE, int FM>
 __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm, int wn, int lane,
-                                         f32x16 (&acc)[2][4]) {
-  constexpr int FM = 2, FN = 4, KG = kPipeRB / 32;
+                                         f32x16 (&acc)[FM][4]) {
+  constexpr int FN = 4, KG = kPipeRB / 32;
   u32x4 af[2][FM], bfr[2][FN];
   load_frags<FM, FN, kPipeRB, kPipeBM, kPipeBNB, MODE>(rd, 0, wm, wn, lane, af[0], bfr[0]);
 #pragma unroll
@@ -471,7 +481,10 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm,
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        acc[fm][fn] = mfma32(E{}, af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
+        // bf16: weights as the 32-row operand (the layout the epilogue wants)
+        acc[fm][fn] = std::is_same<E, ElemBF16>::value
+                          ? mfma32(E{}, bfr[kg & 1][fn], af[kg & 1][fm], acc[fm][fn])
+                          : mfma32(E{}, af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
   }
 }
 
@@ -504,61 +517,102 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
 }
 
-// Epilogue through LDS: the wavefronts write their results as bf16 into a
-// row-major staging tile (16-byte chunks XOR-swizzled by row), then every
-// thread copies whole 16-byte row chunks to global memory.  GEMM2 tiles are
-// 256 columns wide and go out in two halves.  s_dst[r] is the destination
-// row of tile row r (-1: past the expert's last slot), s_gate[r] its gate.
-template <int MODE>
+// Two float32 -> one word of two bfloat16 (hardware round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Epilogue through LDS.  bf16 tiles are multiplied with the MFMA operands
+// swapped (weights as the 32-row operand), so lane l holds token row l % 32
+// of each fragment and, in registers 4j..4j+3, four consecutive output
+// columns 8j + 4(l/32) + 0..3: every lane writes 8-byte runs of a staged
+// row-major bf16 tile (16-byte chunk c of row r at chunk c ^ (r & 15)), then
+// every thread copies whole 16-byte row chunks to global memory.  GEMM2
+// tiles are 256 columns wide and go out in two halves.  s_dst[r] is the
+// destination row of tile row r (-1: past the expert's last slot), s_gate[r]
+// its gate.
+template <int MODE, int FM, int THREADS>
 __device__ __forceinline__ void pipe_store_bf16(const ExpertArgs& a, const Tile& ti, int wm, int wn,
-                                                f32x16 (&acc)[2][4], uint8_t* __restrict__ stage,
+                                                f32x16 (&acc)[FM][4], uint8_t* __restrict__ stage,
                                                 const int* s_dst, const float* s_gate) {
-  constexpr int FM = 2, FN = 4, COLS = 128, CPRW = COLS * 2 / 16;
+  constexpr int FN = 4, COLS = 128, CPRW = COLS * 2 / 16;
   constexpr int PASSES = MODE == 1 ? 1 : 2;
   const int lane = threadIdx.x & 63, lc = lane & 31, lh = lane >> 5;
-  auto lds_off = [&](int row, int col) {
-    const int c = col >> 3;
-    return row * (COLS * 2) + (((c ^ (row & 7)) << 4) | ((col & 7) << 1));
-  };
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
     if (MODE == 1 || wn == pass) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
+        if (FM == 4) {
+          // the accumulators stay in AGPRs up to here: copied to VGPRs one
+          // row fragment at a time, not all at the loop exit
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = (wm * FM + fm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (MODE == 1) {
-#pragma unroll
-            for (int fn = 0; fn < FN / 2; ++fn) {
-              const int col = (wn * (FN / 2) + fn) * 32 + lc;
-              *(uint16_t*)(stage + lds_off(row, col)) =
-                  f32_to_bf16(silu_mul(acc[fm][fn][r], acc[fm][fn + FN / 2][r]));
-            }
-          } else {
-            const float g = s_gate[row];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-              *(uint16_t*)(stage + lds_off(row, fn * 32 + lc)) = f32_to_bf16(acc[fm][fn][r] * g);
-          }
+          for (int fn = 0; fn < FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
         }
+        const int row = (wm * FM + fm) * 32 + lc;
+        uint8_t* rowp = stage + row * (COLS * 2) + lh * 8;
+        const int sw = row & 15;
+        if (MODE == 1) {
+#pragma unroll
+          for (int fn = 0; fn < FN / 2; ++fn)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int c = (wn * (FN / 2) + fn) * 4 + j;
+              const f32x16& gt = acc[fm][fn];
+              const f32x16& up = acc[fm][fn + FN / 2];
+              uint2 w;
+              w.x = pack_bf16x2(silu_mul(gt[4 * j], up[4 * j]), silu_mul(gt[4 * j + 1], up[4 * j + 1]));
+              w.y = pack_bf16x2(silu_mul(gt[4 * j + 2], up[4 * j + 2]),
+                                silu_mul(gt[4 * j + 3], up[4 * j + 3]));
+              *(uint2*)(rowp + ((c ^ sw) << 4)) = w;
+            }
+        } else {
+          const float g = s_gate[row];
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int c = fn * 4 + j;
+              const f32x16& y = acc[fm][fn];
+              uint2 w;
+              w.x = pack_bf16x2(y[4 * j] * g, y[4 * j + 1] * g);
+              w.y = pack_bf16x2(y[4 * j + 2] * g, y[4 * j + 3] * g);
+              *(uint2*)(rowp + ((c ^ sw) << 4)) = w;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     lds_sync();
-    for (int i = threadIdx.x; i < kPipeBM * CPRW; i += kPipeThreads) {
-      const int row = i / CPRW, c = i % CPRW;
-      const int drow = s_dst[row];
-      if (drow < 0) continue;
-      const u32x4 v = *(const u32x4*)(stage + row * (COLS * 2) + ((c ^ (row & 7)) << 4));
-      uint16_t* dst;
-      if (MODE == 1)
-        dst = ti.routed ? (uint16_t*)a.H_routed + (size_t)drow * a.I + ti.n0 + c * 8
-                        : (uint16_t*)a.H_shared + (size_t)drow * a.K_s * a.I +
-                              (size_t)(ti.v - a.N) * a.I + ti.n0 + c * 8;
-      else
-        dst = (ti.routed ? (uint16_t*)a.Y : (uint16_t*)a.Y_shared) + (size_t)drow * a.d + ti.n0 +
-              pass * COLS + c * 8;
-      *(u32x4*)dst = v;
+    // thread t copies chunk t % 16 of rows t / 16 + k * (THREADS / 16)
+    constexpr int RSTEP = THREADS / CPRW, NR = kPipeBM / RSTEP;
+    constexpr int NB = 4;  // rows in flight per thread
+    static_assert(NR % NB == 0, "whole batches");
+    const int c = threadIdx.x % CPRW, r0 = threadIdx.x / CPRW;
+    uint16_t* base;
+    size_t pitch;
+    if (MODE == 1) {
+      base = ti.routed ? (uint16_t*)a.H_routed + ti.n0
+                       : (uint16_t*)a.H_shared + (size_t)(ti.v - a.N) * a.I + ti.n0;
+      pitch = ti.routed ? (size_t)a.I : (size_t)a.K_s * a.I;
+    } else {
+      base = (ti.routed ? (uint16_t*)a.Y : (uint16_t*)a.Y_shared) + ti.n0 + pass * COLS;
+      pitch = (size_t)a.d;
+    }
+#pragma unroll
+    for (int k0 = 0; k0 < NR; k0 += NB) {
+      int drow[NB];
+      u32x4 v[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int row = r0 + (k0 + k) * RSTEP;
+        drow[k] = s_dst[row];
+        v[k] = *(const u32x4*)(stage + row * (COLS * 2) + ((c ^ (row & 15)) << 4));
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (drow[k] >= 0) *(u32x4*)(base + (size_t)drow[k] * pitch + c * 8) = v[k];
     }
     lds_sync();
   }
@@ -583,23 +637,26 @@ __device__ __forceinline__ void pipe_row_dest(const ExpertArgs& a, const Tile& t
   g = a.gate[pair];
 }
 
-template <class E, int MODE>
-__global__ __launch_bounds__(kPipeThreads, 1) void expert_gemm_pipe_kernel(ExpertArgs a) {
+template <class E, int MODE, int W>
+__global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs a) {
   using Tp = typename E::T;
+  using Cfg = PipeCfg<W>;
   constexpr int BNO = MODE == 1 ? kPipeBNB / 2 : kPipeBNB;
   constexpr int kStep = kPipeRB / (int)sizeof(Tp);
-  constexpr int NINST = kPipeNinst;
+  constexpr int NINST = Cfg::kNinst, FM = Cfg::FM;
   constexpr bool kStaged = std::is_same<E, ElemBF16>::value;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kPipeSlot];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kPipeSlot];
   __shared__ int s_tab[kMaxV + 1];
   __shared__ int s_dst[kPipeBM];
-  __shared__ float s_gate[kPipeBM];
+  __shared__ __attribute__((aligned(16))) float s_gate[kPipeBM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int n_a = min(max(kPipeBM / 8 - wave * NINST, 0), NINST);  // this wavefront's A-row loads
+  // wavefronts 0 .. W/2-1 load the A rows, the others the B rows
+  static_assert((kPipeBM / 8) % NINST == 0, "a wavefront loads rows of one operand");
+  const bool is_a = wave * NINST < kPipeBM / 8;
 
   // Persistent: the blocks of XCD x (blockIdx % 8, workgroups are dealt
   // round-robin over the XCDs) walk that XCD's contiguous range of tiles, so
@@ -624,14 +681,19 @@ __global__ __launch_bounds__(kPipeThreads, 1) void expert_gemm_pipe_kernel(Exper
   if (L >= end) return;
 
   Tile ti = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, L));
-  PipeLoads ld;
+  PipeLoads<NINST> ld;
   pipe_prepare<E, MODE>(a, ti, wave, lane, ld);
-  pipe_issue<E, MODE>(a, ti, ld, 0, n_a, lds0 + wave * NINST * 1024);
+  pipe_issue<E, MODE>(a, ti, ld, 0, is_a, lds0 + wave * NINST * 1024);
 
   while (true) {
     const int Kc = MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I);
     const int nsteps = Kc / kStep;  // even (the host only picks this kernel then)
-    const bool active = ti.m0 + wm * 64 < ti.rows;
+    // A wavefront whose rows all lie past the expert's last slot skips its
+    // MFMAs when it shares a SIMD (W = 8); with one wavefront per SIMD (W = 4)
+    // skipping saves no time, and the branch would force the accumulators
+    // out of AGPRs, so every wavefront multiplies (the padded rows repeat
+    // the expert's last slot and are never stored).
+    const bool active = W == 4 || ti.m0 + wm * FM * 32 < ti.rows;
     const int Ln = L + nbx;
     const bool has_next = Ln < end;
     // destination row and gate of tile row `tid`, kept in registers until the epilogue
@@ -639,21 +701,21 @@ __global__ __launch_bounds__(kPipeThreads, 1) void expert_gemm_pipe_kernel(Exper
     float my_gate = 1.f;
     if (tid < kPipeBM) pipe_row_dest<MODE>(a, ti, tid, my_dst, my_gate);
 
-    f32x16 acc[2][4];
+    f32x16 acc[FM][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     Tile tn = ti;
-    PipeLoads ldn = ld;
+    PipeLoads<NINST> ldn = ld;
     for (int s = 0; s < nsteps; s += 2) {
       // even k-step: slot 0 holds k-step s; k-step s + 1 goes to slot 1
       pipe_sync();
-      pipe_issue<E, MODE>(a, ti, ld, s + 1, n_a, lds1 + wave * NINST * 1024);
-      if (active) pipe_mma<E, MODE>(lds0, wm, wn, lane, acc);
+      pipe_issue<E, MODE>(a, ti, ld, s + 1, is_a, lds1 + wave * NINST * 1024);
+      if (active) pipe_mma<E, MODE, FM>(lds0, wm, wn, lane, acc);
       // odd k-step: slot 1 holds k-step s + 1; slot 0 gets k-step s + 2, or
       // the next tile's first k-step after the last one
       if (s + 2 >= nsteps && has_next) {
@@ -662,10 +724,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void expert_gemm_pipe_kernel(Exper
       }
       pipe_sync();
       if (s + 2 < nsteps)
-        pipe_issue<E, MODE>(a, ti, ld, s + 2, n_a, lds0 + wave * NINST * 1024);
+        pipe_issue<E, MODE>(a, ti, ld, s + 2, is_a, lds0 + wave * NINST * 1024);
       else if (has_next)
-        pipe_issue<E, MODE>(a, tn, ldn, 0, n_a, lds0 + wave * NINST * 1024);
-      if (active) pipe_mma<E, MODE>(lds1, wm, wn, lane, acc);
+        pipe_issue<E, MODE>(a, tn, ldn, 0, is_a, lds0 + wave * NINST * 1024);
+      if (active) pipe_mma<E, MODE, FM>(lds1, wm, wn, lane, acc);
     }
 
     // epilogue: slot 1 is free once every wavefront has finished its last reads
@@ -675,9 +737,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void expert_gemm_pipe_kernel(Exper
     }
     lds_sync();
     if constexpr (kStaged) {
-      pipe_store_bf16<MODE>(a, ti, wm, wn, acc, lds1, s_dst, s_gate);
+      pipe_store_bf16<MODE, FM, Cfg::kThreads>(a, ti, wm, wn, acc, lds1, s_dst, s_gate);
     } else {
-      store_tile<E, MODE, 2, 4>(a, ti, wm, wn, acc);
+      store_tile<E, MODE, FM, 4>(a, ti, wm, wn, acc);
       __syncthreads();
     }
     if (!has_next) break;
@@ -705,6 +767,15 @@ bool force_reg() {
     return (e != nullptr && !strcmp(e, "reg")) ? 1 : 0;
   }();
   return v != 0;
+}
+
+// MOE_GEMM_VARIANT=pipe4 selects the four-wavefront pipelined kernel.
+int pipe_waves() {
+  static int v = [] {
+    const char* e = getenv("MOE_GEMM_VARIANT");
+    return (e != nullptr && !strcmp(e, "pipe4")) ? 4 : 8;
+  }();
+  return v;
 }
 
 // The pipelined kernel needs 128-column H tiles (I % 128), 256-column Y tiles
@@ -755,13 +826,13 @@ int cu_count() {
   return cache[dev];
 }
 
-template <class E, int MODE>
+template <class E, int MODE, int W>
 hipError_t launch_pipe(const ExpertArgs& a, hipStream_t st) {
   constexpr int BNO = MODE == 1 ? kPipeBNB / 2 : kPipeBNB;
   long long g = grid_tiles(a, kPipeBM, (MODE == 1 ? a.I : a.d) / BNO, MODE);
   if (g <= 0) return hipSuccess;
   g = std::min<long long>(g, (long long)cu_count());  // persistent: one block per CU
-  expert_gemm_pipe_kernel<E, MODE><<<dim3((unsigned)g), dim3(kPipeThreads), 0, st>>>(a);
+  expert_gemm_pipe_kernel<E, MODE, W><<<dim3((unsigned)g), dim3(PipeCfg<W>::kThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -769,7 +840,13 @@ template <class E, int MODE>
 hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
   const int es = (int)sizeof(typename E::T);
   const Shape s = MODE == 1 ? shape1(a, es) : shape2(a, es);
-  if (s.kind == 1) return launch_pipe<E, MODE>(a, st);
+  if (s.kind == 1) {
+    // float32 keeps eight wavefronts (its four-wavefront build spills)
+    if constexpr (std::is_same<E, ElemF32>::value)
+      return launch_pipe<E, MODE, 8>(a, st);
+    else
+      return pipe_waves() == 8 ? launch_pipe<E, MODE, 8>(a, st) : launch_pipe<E, MODE, 4>(a, st);
+  }
   if (MODE == 1) {
     if (s.WM == 1) return launch_reg<E, 1, 4, 1, 2, 1>(a, st);
     if (s.FM == 1) return launch_reg<E, 2, 2, 1, 2, 1>(a, st);

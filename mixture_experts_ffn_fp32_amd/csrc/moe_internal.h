@@ -11,6 +11,7 @@ using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 using f32x4 = float __attribute__((ext_vector_type(4)));
 using f32x16 = float __attribute__((ext_vector_type(16)));
 using bf16x8 = __bf16 __attribute__((ext_vector_type(8)));
+using bf16x2 = __bf16 __attribute__((ext_vector_type(2)));
 
 // Element traits: storage type and how many elements one 16-byte chunk holds.
 struct ElemF32 {
