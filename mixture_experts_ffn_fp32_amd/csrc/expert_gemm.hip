@@ -452,28 +452,62 @@ __device__ __forceinline__ void pipe_prepare(const ExpertArgs& a, const Tile& ti
   }
 }
 
+// Wavefront-uniform global base of this wavefront's rows at k-step s.
 template <class E, int MODE, int NI>
-__device__ __forceinline__ void pipe_issue(const ExpertArgs& a, const Tile& ti,
-                                           const PipeLoads<NI>& ld, int s, bool is_a,
-                                           uint8_t* __restrict__ wr) {
+__device__ __forceinline__ const uint8_t* pipe_dma_base(const ExpertArgs& a, const Tile& ti,
+                                                        const PipeLoads<NI>& ld, int s, bool is_a) {
   using Tp = typename E::T;
   constexpr int kStep = kPipeRB / (int)sizeof(Tp);
   const size_t k0 = (size_t)s * kStep;
   const uint8_t* ab = ld.a_base + k0 * sizeof(Tp);
   const uint8_t* bb = ld.b_row0 + b_offset<MODE>(a, ti, k0) * sizeof(Tp);
-  dma_fill<NI>(wr, uni(is_a ? ab : bb), ld.off);
+  return uni(is_a ? ab : bb);
 }
 
-// Multiplies one k-step out of slot `rd` (fragments of the next 16-k group are
-// read while the current one is on the MFMA pipe).
-template <class E, int MODE, int FM>
+template <class E, int MODE, int NI>
+__device__ __forceinline__ void pipe_issue(const ExpertArgs& a, const Tile& ti,
+                                           const PipeLoads<NI>& ld, int s, bool is_a,
+                                           uint8_t* __restrict__ wr) {
+  dma_fill<NI>(wr, pipe_dma_base<E, MODE>(a, ti, ld, s, is_a), ld.off);
+}
+
+// The k-groups of one k-step that also issue the other slot's loads.
+#ifndef MOE_DMA_GROUPS
+#define MOE_DMA_GROUPS 2
+#endif
+#ifndef MOE_SCHED_PATTERN
+#define MOE_SCHED_PATTERN 1
+#endif
+
+// Multiplies one k-step out of slot `rd` and issues the direct-to-LDS loads
+// of the other slot (base `db`, lane offsets `off`, into `wr`).  The
+// instruction stream is laid out explicitly: the fragments of k-group g + 1
+// are read from LDS, and the loads issued, one instruction after each MFMA
+// of group g, so neither the LDS latency nor a burst of loads holds the
+// MFMAs back.  A wavefront whose rows are all padding (`active` false) only
+// issues its loads.
+template <class E, int MODE, int FM, int NI>
 __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm, int wn, int lane,
-                                         f32x16 (&acc)[FM][4]) {
-  constexpr int FN = 4, KG = kPipeRB / 32;
+                                         f32x16 (&acc)[FM][4], bool active,
+                                         const uint8_t* db, const uint32_t (&off)[NI],
+                                         uint8_t* __restrict__ wr) {
+  constexpr int FN = 4, KG = kPipeRB / 32, PARTS = MOE_DMA_GROUPS, PER = NI / PARTS;
+  static_assert(NI % PARTS == 0 && PARTS <= KG, "DMA parts");
+  if (!active) {
+    dma_fill<NI>(wr, db, off);
+    return;
+  }
   u32x4 af[2][FM], bfr[2][FN];
   load_frags<FM, FN, kPipeRB, kPipeBM, kPipeBNB, MODE>(rd, 0, wm, wn, lane, af[0], bfr[0]);
 #pragma unroll
   for (int kg = 0; kg < KG; ++kg) {
+    if (kg < PARTS) {
+#pragma unroll
+      for (int i = kg * PER; i < (kg + 1) * PER; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(db + off[i]),
+                                         (__attribute__((address_space(3))) void*)(wr + i * 1024),
+                                         16, 0, 0);
+    }
     if (kg + 1 < KG)
       load_frags<FM, FN, kPipeRB, kPipeBM, kPipeBNB, MODE>(rd, kg + 1, wm, wn, lane,
                                                             af[(kg + 1) & 1], bfr[(kg + 1) & 1]);
@@ -486,6 +520,21 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm,
                           ? mfma32(E{}, bfr[kg & 1][fn], af[kg & 1][fm], acc[fm][fn])
                           : mfma32(E{}, af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
   }
+#if MOE_SCHED_PATTERN
+  // the layout: group 0's fragment reads first, then per k-group g its MFMAs,
+  // each followed by one of group g + 1's reads and one of its loads
+  __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg) {
+    const int nr = kg + 1 < KG ? FM + FN : 0, nd = kg < PARTS ? PER : 0;
+#pragma unroll
+    for (int m = 0; m < FM * FN; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (m < nd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  }
+#endif
 }
 
 // s_waitcnt vmcnt(0) lgkmcnt(0), then a barrier without memory fences (the
@@ -710,24 +759,25 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     Tile tn = ti;
-    PipeLoads<NINST> ldn = ld;
     for (int s = 0; s < nsteps; s += 2) {
       // even k-step: slot 0 holds k-step s; k-step s + 1 goes to slot 1
       pipe_sync();
-      pipe_issue<E, MODE>(a, ti, ld, s + 1, is_a, lds1 + wave * NINST * 1024);
-      if (active) pipe_mma<E, MODE, FM>(lds0, wm, wn, lane, acc);
+      pipe_mma<E, MODE, FM>(lds0, wm, wn, lane, acc, active,
+                            pipe_dma_base<E, MODE>(a, ti, ld, s + 1, is_a), ld.off,
+                            lds1 + wave * NINST * 1024);
       // odd k-step: slot 1 holds k-step s + 1; slot 0 gets k-step s + 2, or
       // the next tile's first k-step after the last one
       if (s + 2 >= nsteps && has_next) {
         tn = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, Ln));
-        pipe_prepare<E, MODE>(a, tn, wave, lane, ldn);
+        pipe_prepare<E, MODE>(a, tn, wave, lane, ld);  // this tile's loads are all issued
       }
       pipe_sync();
-      if (s + 2 < nsteps)
-        pipe_issue<E, MODE>(a, ti, ld, s + 2, is_a, lds0 + wave * NINST * 1024);
-      else if (has_next)
-        pipe_issue<E, MODE>(a, tn, ldn, 0, is_a, lds0 + wave * NINST * 1024);
-      if (active) pipe_mma<E, MODE, FM>(lds1, wm, wn, lane, acc);
+      // after the last k-step: the next tile's first k-step, or (last tile)
+      // the first k-step again into the slot nobody reads any more
+      const uint8_t* db2 = s + 2 < nsteps ? pipe_dma_base<E, MODE>(a, ti, ld, s + 2, is_a)
+                                          : pipe_dma_base<E, MODE>(a, tn, ld, 0, is_a);
+      pipe_mma<E, MODE, FM>(lds1, wm, wn, lane, acc, active, uni(db2), ld.off,
+                            lds0 + wave * NINST * 1024);
     }
 
     // epilogue: slot 1 is free once every wavefront has finished its last reads
@@ -742,10 +792,12 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
       store_tile<E, MODE, FM, 4>(a, ti, wm, wn, acc);
       __syncthreads();
     }
-    if (!has_next) break;
+    if (!has_next) {
+      MOE_WAIT_VMCNT(0);  // the spare reload into slot 0 lands before the block ends
+      break;
+    }
     L = Ln;
     ti = tn;
-    ld = ldn;
   }
 }
 
