@@ -357,6 +357,27 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n)&0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
 #define MOE_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14))
+#ifndef MOE_DMA_BUFFER
+#define MOE_DMA_BUFFER 1
+#endif
+
+// One direct-to-LDS load: 16 bytes per lane from `base` + `off` (base
+// wavefront-uniform) to LDS `wr` + 16 * lane.  It is issued as a buffer load
+// (MUBUF) rather than a global one: the compiler counts a global (FLAT)
+// direct-to-LDS load as a possible LDS access of unknown order and then
+// waits for every outstanding LDS read (lgkmcnt(0)) before each MFMA that
+// needs one; buffer loads keep its partial lgkmcnt waits exact.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* __restrict__ wr) {
+#if MOE_DMA_BUFFER
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wr, 16, off,
+                                           0, 0, 0);
+#else
+  __builtin_amdgcn_global_load_lds((const void*)(base + off),
+                                   (__attribute__((address_space(3))) void*)wr, 16, 0, 0);
+#endif
+}
 
 // Direct-to-LDS loads of one k-step of this lane's rows into `wr` (every row
 // of a wavefront belongs to the same operand, so `base` is wavefront-uniform
@@ -368,10 +389,7 @@ template <int NINST>
 __device__ __forceinline__ void dma_fill(uint8_t* __restrict__ wr, const uint8_t* base,
                                          const uint32_t (&off)[NINST]) {
 #pragma unroll
-  for (int i = 0; i < NINST; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
-                                     (__attribute__((address_space(3))) void*)(wr + i * 1024), 16,
-                                     0, 0);
+  for (int i = 0; i < NINST; ++i) dma16(base, off[i], wr + i * 1024);
 }
 
 template <int FM, int FN, int RB, int BM, int BNB, int MODE>
@@ -503,10 +521,7 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm,
   for (int kg = 0; kg < KG; ++kg) {
     if (kg < PARTS) {
 #pragma unroll
-      for (int i = kg * PER; i < (kg + 1) * PER; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(db + off[i]),
-                                         (__attribute__((address_space(3))) void*)(wr + i * 1024),
-                                         16, 0, 0);
+      for (int i = kg * PER; i < (kg + 1) * PER; ++i) dma16(db, off[i], wr + i * 1024);
     }
     if (kg + 1 < KG)
       load_frags<FM, FN, kPipeRB, kPipeBM, kPipeBNB, MODE>(rd, kg + 1, wm, wn, lane,
