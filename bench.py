@@ -201,7 +201,8 @@ def main():
         dinp = moe_inputs.make(args.decode_workload)
         dw = dinp.w
         dt_ = upload(dinp, dev)
-        dms, dstages = time_layer(mx, dt_, dw, args.decode_steps, 10, False)
+        dms, _ = time_layer(mx, dt_, dw, args.decode_steps, 10, False)
+        _, dstages = time_layer(mx, dt_, dw, 20, 2, True)
         hit = experts_hit(mx, dt_, dw)
         es = 2 if dw.dtype == "bf16" else 4
         dbytes = ((hit + dw.K_s) * 3 * dw.d * dw.I * es + dw.N * dw.d * es
@@ -210,7 +211,9 @@ def main():
         decode = {"workload": dw.name, "tokens_per_s": round(dw.T / dstep, 1),
                   "ms_per_step": round(dstep * 1e3, 4), "experts_hit": hit,
                   "algorithmic_bytes": dbytes, "hbm_GBs": round(dbytes / dstep / 1e9, 1),
-                  "hbm_frac": round(dbytes / dstep / 1e9 / PEAK_HBM_GBS, 4)}
+                  "hbm_frac": round(dbytes / dstep / 1e9 / PEAK_HBM_GBS, 4),
+                  "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in dstages.items()
+                               if v[1]}}
         del dt_
         torch.cuda.empty_cache()
 

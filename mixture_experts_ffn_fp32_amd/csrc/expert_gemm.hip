@@ -816,11 +816,215 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   }
 }
 
+// ---------------------------------------------------------------- weight-streaming kernel
+// Decode-sized batches (a few tokens per expert) are bound by streaming the
+// weights of every selected expert once, so this kernel keeps as many bytes
+// in flight per CU as LDS allows.  Tiles are 32 rows (slots of one expert)
+// x 128 B rows (GEMM1: gate and up rows of 64 columns, interleaved in runs
+// of 32; GEMM2: 128 output columns), one 128-byte k-step of every row per
+// ring slot, kStrS slots.  The block is persistent and walks its tiles as
+// one sequence of k-steps.  Wavefronts 2 and 3 only load: they keep the
+// next kStrS - 1 k-steps in flight with direct-to-LDS buffer loads, wait for
+// the oldest with an exact vmcnt (they issue nothing else), and release it
+// with a barrier.  Wavefronts 0 and 1 only compute: after each barrier they
+// multiply the released slot (each owns 64 of the 128 B rows) and, at the
+// end of a tile, write its rows.
+constexpr int kStrBM = 32, kStrBR = 128, kStrS = 6;
+constexpr int kStrRows = kStrBM + kStrBR;
+constexpr int kStrSlot = kStrRows * 128;
+constexpr int kStrNI = kStrRows / 8 / 2;  // loads per loading wavefront per k-step
+
+template <int MODE>
+__host__ __device__ __forceinline__ int str_nt(const ExpertArgs& a) {
+  return MODE == 1 ? a.I / (kStrBR / 2) : a.d / kStrBR;
+}
+
+// Row r of a stream tile at contraction index 0: A rows 0..31, B rows after.
+template <int MODE>
+__device__ __forceinline__ const uint16_t* str_row_ptr(const ExpertArgs& a, const Tile& ti, int r) {
+  if (r < kStrBM) return (const uint16_t*)tile_row_ptr<ElemBF16, MODE, kStrBM, kStrBR>(a, ti, r);
+  const int rb = r - kStrBM;
+  const size_t Id = (size_t)a.I * a.d;
+  const uint16_t* W = ti.routed ? (const uint16_t*)a.W_routed + (size_t)ti.v * 3 * Id
+                                : (const uint16_t*)a.W_shared +
+                                      (size_t)(MODE == 1 ? ti.v - a.N : 0) * 3 * Id;
+  if (MODE == 1) {
+    const int q = rb >> 5, col = ti.n0 + (q >> 1) * 32 + (rb & 31);  // runs: gate, up, gate, up
+    return W + ((q & 1) ? Id : 0) + (size_t)col * a.d;
+  }
+  return W + 2 * Id + (size_t)(ti.n0 + rb) * a.I;
+}
+
+// Steps of tile L and its geometry.
+template <int MODE>
+__device__ __forceinline__ int str_steps(const ExpertArgs& a, const Tile& ti) {
+  return (MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I)) / 64;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void expert_gemm_stream_kernel(ExpertArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStrS * kStrSlot];
+  __shared__ int s_tab[kMaxV + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int V = load_tile_table<MODE>(a, s_tab);
+  const int nt = str_nt<MODE>(a);
+  const int total = s_tab[V] * nt;
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= total) return;  // whole block: no barrier is left behind
+  // the block's k-steps, over its tiles blockIdx.x, + G, ...
+  int nsteps_all = 0;
+  for (int L = blockIdx.x; L < total; L += G)
+    nsteps_all += str_steps<MODE>(a, tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+
+  if (wave >= 2) {
+    // ---- loading wavefronts: rows (wave - 2) * 80 .. + 79 of each slot
+    const int w2 = wave - 2;
+    int L = blockIdx.x, s = 0;
+    Tile ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+    int ns = str_steps<MODE>(a, ti);
+    uint32_t off[kStrNI];
+    const uint8_t* a_base = nullptr;
+    const uint8_t* b_base = nullptr;
+    auto prepare = [&]() {
+      b_base = uni((const uint8_t*)str_row_ptr<MODE>(a, ti, kStrBM));
+      a_base = uni(MODE == 1 ? (const uint8_t*)a.u
+                             : (const uint8_t*)(ti.routed ? a.H_routed : a.H_shared));
+#pragma unroll
+      for (int i = 0; i < kStrNI; ++i) {
+        const int r = (w2 * kStrNI + i) * 8 + (lane >> 3);
+        const uint8_t* rp = (const uint8_t*)str_row_ptr<MODE>(a, ti, r);
+        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+        off[i] = (uint32_t)(rp - (r < kStrBM ? a_base : b_base)) + chunk * 16;
+      }
+    };
+    prepare();
+    // issue the loads of the cursor's k-step into slot `slot`, then advance
+    // the cursor (past the block's last k-step it stays there: the spare
+    // loads reread valid memory into slots nobody reads any more)
+    auto issue = [&](int slot) {
+      const size_t k0 = (size_t)s * 64;
+      const uint8_t* ab = uni(a_base + k0 * 2);
+      const uint8_t* bb = uni(b_base + b_offset<MODE>(a, ti, k0) * 2);
+      uint8_t* wr = ring + slot * kStrSlot + w2 * kStrNI * 1024;
+#pragma unroll
+      for (int i = 0; i < kStrNI; ++i) {
+        const bool is_a = (w2 * kStrNI + i) * 8 < kStrBM;  // whole instruction: 8 rows
+        dma16(is_a ? ab : bb, off[i], wr + i * 1024);
+      }
+      if (s + 1 < ns) {
+        ++s;
+      } else if (L + G < total) {
+        L += G;
+        s = 0;
+        ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+        ns = str_steps<MODE>(a, ti);
+        prepare();
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < kStrS - 1; ++j) issue(j);
+    int slot = kStrS - 1;
+    for (int g = 0; g < nsteps_all; ++g) {
+      MOE_WAIT_VMCNT((kStrS - 2) * kStrNI);  // k-step g has landed
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(slot);  // k-step g + kStrS - 1 into the slot read at k-step g - 1
+      slot = slot + 1 == kStrS ? 0 : slot + 1;
+    }
+    MOE_WAIT_VMCNT(0);
+    return;
+  }
+
+  // ---- computing wavefronts: B rows wave * 64 .. + 63 (two 32-row fragments)
+  const int lc = lane & 31, lh = lane >> 5;
+  int L = blockIdx.x, s = 0, slot = 0;
+  Tile ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+  int ns = str_steps<MODE>(a, ti);
+  f32x16 acc[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[f][r] = 0.f;
+  for (int g = 0; g < nsteps_all; ++g) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint8_t* rd = ring + slot * kStrSlot;
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const int ch = kg * 2 + lh;
+      const u32x4 af = *(const u32x4*)(rd + lds_chunk_offset(lc, ch));
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const u32x4 bf = *(const u32x4*)(rd + lds_chunk_offset(kStrBM + wave * 64 + f * 32 + lc, ch));
+        acc[f] = mfma32(ElemBF16{}, bf, af, acc[f]);  // lane = token row
+      }
+    }
+    MOE_WAIT_LGKMCNT0();  // this slot's reads are done before the next barrier
+    slot = slot + 1 == kStrS ? 0 : slot + 1;
+    if (++s < ns) continue;
+    // ---- end of tile: lane holds row m0 + lc, columns 8j + 4 lh + 0..3 of each fragment
+    const int p = ti.m0 + lc;
+    if (p < ti.rows) {
+      if (MODE == 1) {
+        uint16_t* dst = ti.routed ? (uint16_t*)a.H_routed + (size_t)(ti.row_base + p) * a.I
+                                  : (uint16_t*)a.H_shared + (size_t)p * a.K_s * a.I +
+                                        (size_t)(ti.v - a.N) * a.I;
+        dst += ti.n0 + wave * 32 + 4 * lh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint2 w;
+          w.x = pack_bf16x2(silu_mul(acc[0][4 * j], acc[1][4 * j]),
+                            silu_mul(acc[0][4 * j + 1], acc[1][4 * j + 1]));
+          w.y = pack_bf16x2(silu_mul(acc[0][4 * j + 2], acc[1][4 * j + 2]),
+                            silu_mul(acc[0][4 * j + 3], acc[1][4 * j + 3]));
+          *(uint2*)(dst + 8 * j) = w;
+        }
+      } else {
+        float gt = 1.f;
+        uint16_t* dst;
+        if (ti.routed) {
+          const int TK = a.T * a.K;
+          int pair = a.sorted_pair[ti.row_base + p];
+          pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
+          gt = a.gate[pair];
+          dst = (uint16_t*)a.Y + (size_t)pair * a.d;
+        } else {
+          dst = (uint16_t*)a.Y_shared + (size_t)p * a.d;
+        }
+        dst += ti.n0 + wave * 64 + 4 * lh;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[f][4 * j] * gt, acc[f][4 * j + 1] * gt);
+            w.y = pack_bf16x2(acc[f][4 * j + 2] * gt, acc[f][4 * j + 3] * gt);
+            *(uint2*)(dst + f * 32 + 8 * j) = w;
+          }
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[f][r] = 0.f;
+    s = 0;
+    L += G;
+    if (L < total) {
+      ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+      ns = str_steps<MODE>(a, ti);
+    }
+  }
+}
+
 // Kernel choice.  kind 0: register-staged kernel with wavefronts WM x WN and
-// 32x32 fragments FM x FN per wavefront; kind 1: the pipelined LDS-DMA kernel.
+// 32x32 fragments FM x FN per wavefront; kind 1: the pipelined LDS-DMA
+// kernel; kind 2: the weight-streaming kernel (bf16, decode-sized batches).
 struct Shape {
   int kind, WM, WN, FM, FN;
-  int bm() const { return kind == 1 ? kPipeBM : WM * FM * 32; }
+  int bm() const { return kind == 1 ? kPipeBM : kind == 2 ? kStrBM : WM * FM * 32; }
 };
 
 // Few tokens per expert (decode-sized batches): short M tiles, wide N tiles,
@@ -851,11 +1055,13 @@ bool pipe_ok1(const ExpertArgs& a, int es) { return a.I % 128 == 0 && (a.d * es)
 bool pipe_ok2(const ExpertArgs& a, int es) { return a.d % 256 == 0 && (a.I * es) % 256 == 0; }
 
 Shape shape1(const ExpertArgs& a, int es) {
+  if (small_m(a) && es == 2 && !force_reg()) return Shape{2, 0, 0, 0, 0};
   if (small_m(a)) return a.I % 128 == 0 ? Shape{0, 1, 4, 1, 2} : Shape{0, 2, 2, 1, 2};
   if (!force_reg() && pipe_ok1(a, es)) return Shape{1, 4, 2, 2, 4};
   return Shape{0, 2, 2, 2, 2};
 }
 Shape shape2(const ExpertArgs& a, int es) {
+  if (small_m(a) && es == 2 && !force_reg() && a.d % kStrBR == 0) return Shape{2, 0, 0, 0, 0};
   if (small_m(a)) return a.d % 256 == 0 ? Shape{0, 1, 4, 1, 2} : Shape{0, 2, 2, 1, 1};
   if (!force_reg() && pipe_ok2(a, es)) return Shape{1, 4, 2, 2, 4};
   return a.d % 128 == 0 ? Shape{0, 2, 2, 2, 2} : Shape{0, 2, 2, 2, 1};
@@ -903,10 +1109,21 @@ hipError_t launch_pipe(const ExpertArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int MODE>
+hipError_t launch_stream(const ExpertArgs& a, hipStream_t st) {
+  long long g = grid_tiles(a, kStrBM, str_nt<MODE>(a), MODE);
+  if (g <= 0) return hipSuccess;
+  g = std::min<long long>(g, (long long)cu_count());  // persistent: one block per CU
+  expert_gemm_stream_kernel<MODE><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <class E, int MODE>
 hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
   const int es = (int)sizeof(typename E::T);
   const Shape s = MODE == 1 ? shape1(a, es) : shape2(a, es);
+  if constexpr (std::is_same<E, ElemBF16>::value)
+    if (s.kind == 2) return launch_stream<MODE>(a, st);
   if (s.kind == 1) {
     // float32 keeps eight wavefronts (its four-wavefront build spills)
     if constexpr (std::is_same<E, ElemF32>::value)

@@ -5,18 +5,39 @@
 // largest s of each token are kept as its gates, the rest are zero.  Ties
 // are broken towards the lower expert index so that exactly K are kept.
 //
-// Layout of the work: one block = 64 tokens = 4 wavefronts x 16 tokens.  A
+// Layout of the work: one block = 64 tokens = 4 wavefronts x 16 tokens.
+// Token rows and expert rows are staged through two LDS buffers, up to 512
+// bytes of each row per stage.  A
 // wavefront computes the logits of its 16 tokens against all N experts
 // (padded to 16F) with 16x16 MFMA tiles, then each group of 16 lanes owns one
 // token at a time (the MFMA output puts token rows on lane groups and
 // experts on lanes), so softmax and top-K reductions are 4-step butterflies
 // inside a 16-lane group.  Logits never leave registers.
+#include <cstdlib>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTokens = 64;
+
+// Lane exchange inside a row of 16 lanes through DPP (no LDS round trip), a
+// butterfly: step 0 pairs lanes i and i ^ 1, step 1 i and i ^ 2 (quad
+// permutations), step 2 i and i ^ 7 (half-row mirror: quad 0 with quad 1,
+// quad 2 with quad 3), step 3 i and i ^ 15 (row mirror: half 0 with half 1).
+// Every step combines two equal-sized partial results that the partner lane
+// holds bit for bit, so after the four steps every lane of the row has the
+// same combination of all 16 values, with the same bits (the combining
+// operations being commutative).
+template <int STEP>
+__device__ __forceinline__ int row16_exchange(int v) {
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
+}
+template <int STEP>
+__device__ __forceinline__ float row16_exchange(float v) {
+  return __int_as_float(row16_exchange<STEP>(__float_as_int(v)));
+}
 
 __device__ __forceinline__ f32x4 mfma16(ElemBF16, u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -31,7 +52,23 @@ __device__ __forceinline__ f32x4 mfma16(ElemF32, u32x4 a, u32x4 b, f32x4 c) {
   return c;
 }
 
-template <class E, int F>
+// LDS slot of 16-byte chunk c of row r when a row holds CH chunks: rows of
+// 128 bytes pair up in one 256-byte bank window (chunk c ^ ((r >> 1) & 7));
+// longer rows rotate over 16 chunks (c ^ (r & 15)).  16 lanes reading one
+// chunk of 16 consecutive rows then hit 16 distinct bank groups.
+template <int CH>
+__device__ __forceinline__ int router_lds_offset(int r, int c) {
+  if (CH == 8) return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+  return r * (CH * 16) + ((c ^ (r & 15)) << 4);
+}
+
+// F: experts padded to 16F.  CH: 16-byte chunks of each row loaded per
+// k-step (long k-steps keep many loads in flight per wavefront: the kernel
+// is bound by the latency of reading u once).  TB: tokens per block; the
+// 4 wavefronts form 4 / WG groups of 16 tokens, the WG = 64 / TB wavefronts
+// of a group share its expert fragments (f % WG) and meet in LDS for the
+// softmax, which the group's first wavefront computes.
+template <class E, int F, int CH, int TB>
 __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __restrict__ u,
                                                      const typename E::T* __restrict__ Eg,
                                                      const float* __restrict__ bias, int T, int d,
@@ -40,41 +77,44 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
                                                      float* __restrict__ scores) {
   using Tp = typename E::T;
   constexpr int NP = 16 * F;            // experts, padded
-  constexpr int ROWS = kTokens + NP;    // LDS rows per stage: tokens, then experts
-  constexpr int PASSES = (ROWS + 31) / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][ROWS * 128];
+  constexpr int ROWS = TB + NP;         // LDS rows per stage: tokens, then experts
+  constexpr int WG = 64 / TB;           // wavefronts per group of 16 tokens
+  constexpr int RPP = 256 / CH;         // rows covered by one pass of the block
+  constexpr int PASSES = (ROWS + RPP - 1) / RPP;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][ROWS * CH * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * kTokens;
-  constexpr int kStep = 128 / (int)sizeof(Tp);  // contraction elements per stage
+  const int t0 = blockIdx.x * TB;
+  const int tg = wave / WG, wr = wave % WG;  // token group, rank inside it
+  constexpr int kStep = CH * E::kPerChunk;  // contraction elements per stage
   const int nsteps = d / kStep;
 
-  // Each thread moves chunk c of rows tid/8 + 32*i.  Rows past T or N are
-  // clamped to a valid row; their results are never written.
-  const int c = tid & 7;
+  // Each thread moves chunk c of rows tid / CH + RPP * i.  Rows past T or N
+  // are clamped to a valid row; their results are never written.
+  const int c = tid % CH;
   const Tp* rowp[PASSES];
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    if (r < kTokens) {
+    const int r = tid / CH + RPP * i;
+    if (r < TB) {
       rowp[i] = u + (size_t)min(t0 + r, T - 1) * d;
     } else {
-      rowp[i] = Eg + (size_t)min(r - kTokens, N - 1) * d;
+      rowp[i] = Eg + (size_t)min(max(r - TB, 0), N - 1) * d;
     }
   }
   u32x4 stage[PASSES];
   auto gload = [&](int s) {
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
-      const int r = (tid >> 3) + 32 * i;
+      const int r = tid / CH + RPP * i;
       if (r < ROWS) stage[i] = *(const u32x4*)(rowp[i] + s * kStep + c * E::kPerChunk);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      if (r < ROWS) *(u32x4*)(lds[buf] + lds_chunk_offset(r, c)) = stage[i];
+      const int r = tid / CH + RPP * i;
+      if (r < ROWS) *(u32x4*)(lds[buf] + router_lds_offset<CH>(r, c)) = stage[i];
     }
   };
 
@@ -89,13 +129,14 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
     const int buf = s & 1;
     if (s + 1 < nsteps) gload(s + 1);
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {  // a 128-byte row = two k-groups of 4 chunks
+    for (int kg = 0; kg < CH / 4; ++kg) {  // k-groups of 4 chunks
       const int ch = kg * 4 + (lane >> 4);
-      const u32x4 a = *(const u32x4*)(lds[buf] + lds_chunk_offset(wave * 16 + (lane & 15), ch));
+      const u32x4 a = *(const u32x4*)(lds[buf] + router_lds_offset<CH>(tg * 16 + (lane & 15), ch));
 #pragma unroll
       for (int f = 0; f < F; ++f) {
+        if (WG > 1 && f % WG != wr) continue;
         const u32x4 b =
-            *(const u32x4*)(lds[buf] + lds_chunk_offset(kTokens + f * 16 + (lane & 15), ch));
+            *(const u32x4*)(lds[buf] + router_lds_offset<CH>(TB + f * 16 + (lane & 15), ch));
         acc[f] = mfma16(E{}, a, b, acc[f]);
       }
     }
@@ -103,11 +144,26 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
     __syncthreads();
   }
 
-  // acc[f][r]: token row wave*16 + 4*(lane/16) + r, expert f*16 + lane%16.
+  // acc[f][r]: token row tg*16 + 4*(lane/16) + r, expert f*16 + lane%16.
   const int grp = lane >> 4, col = lane & 15;
+  if constexpr (WG > 1) {
+    // the group's fragments meet in LDS (the ring is free after the last barrier)
+    float* lg = (float*)&lds[0][0] + tg * 16 * NP;
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+      if (f % WG == wr)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lg[(grp * 4 + r) * NP + f * 16 + col] = acc[f][r];
+    __syncthreads();
+    if (wr != 0) return;
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[f][r] = lg[(grp * 4 + r) * NP + f * 16 + col];
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int t = t0 + wave * 16 + grp * 4 + r;
+    const int t = t0 + tg * 16 + grp * 4 + r;
     float v[F];
     float m = -INFINITY;
 #pragma unroll
@@ -116,8 +172,10 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
       v[f] = (e < N) ? acc[f][r] + (bias ? bias[e] : 0.f) : -INFINITY;
       m = fmaxf(m, v[f]);
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    m = fmaxf(m, row16_exchange<0>(m));
+    m = fmaxf(m, row16_exchange<1>(m));
+    m = fmaxf(m, row16_exchange<2>(m));
+    m = fmaxf(m, row16_exchange<3>(m));
     float sum = 0.f;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
@@ -125,9 +183,11 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
       v[f] = (e < N) ? expf(v[f] - m) : 0.f;
       sum += v[f];
     }
-    // xor butterfly: every lane of the group ends with the bit-identical sum
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o);
+    // every lane of the group ends with the bit-identical sum
+    sum += row16_exchange<0>(sum);
+    sum += row16_exchange<1>(sum);
+    sum += row16_exchange<2>(sum);
+    sum += row16_exchange<3>(sum);
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int e = f * 16 + col;
@@ -144,15 +204,16 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
           bi = f * 16 + col;
         }
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
+      auto take = [&](float ov, int oi) {
         if (ov > bv || (ov == bv && oi < bi)) {
           bv = ov;
           bi = oi;
         }
-      }
+      };
+      take(row16_exchange<0>(bv), row16_exchange<0>(bi));
+      take(row16_exchange<1>(bv), row16_exchange<1>(bi));
+      take(row16_exchange<2>(bv), row16_exchange<2>(bi));
+      take(row16_exchange<3>(bv), row16_exchange<3>(bi));
 #pragma unroll
       for (int f = 0; f < F; ++f)
         if (f * 16 + col == bi) v[f] = -1.f;  // taken (-1 is below every score)
@@ -164,24 +225,53 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
   }
 }
 
+template <class E, int F, int TB>
+hipError_t launch_router_tb(const void* u, const void* Eg, const float* bias, int T, int d, int N,
+                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
+  using Tp = typename E::T;
+  const dim3 grid((T + TB - 1) / TB), block(256);
+  const Tp* up = (const Tp*)u;
+  const Tp* ep = (const Tp*)Eg;
+  // long k-steps (two stages of (TB + 16F) rows in LDS) where d allows
+  constexpr int CH = F <= 4 ? 32 : F == 8 ? 16 : 8;
+  if ((size_t)d * sizeof(Tp) % (CH * 16) == 0)
+    router_kernel<E, F, CH, TB><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
+  else
+    router_kernel<E, F, 8, TB><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
+  return hipGetLastError();
+}
+
+// Tokens per block: 64 (measured fastest at both the decode and the prefill
+// sizes: each block is bound by the latency of its k-steps, not by the
+// number of blocks).  MOE_ROUTER_TB=16 or 32 selects the expert-split
+// layouts (tuning runs; results are identical).
+int router_tb(int T) {
+  (void)T;
+  static const int v = [] {
+    const char* e = getenv("MOE_ROUTER_TB");
+    return e == nullptr ? 64 : atoi(e) == 16 ? 16 : atoi(e) == 32 ? 32 : 64;
+  }();
+  return v;
+}
+
+template <class E, int F>
+hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int T, int d, int N,
+                           int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
+  switch (router_tb(T)) {
+    case 16: return launch_router_tb<E, F, 16>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
+    case 32: return launch_router_tb<E, F, 32>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
+    default: return launch_router_tb<E, F, 64>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
+  }
+}
+
 template <class E>
 hipError_t launch_router_t(const void* u, const void* Eg, const float* bias, int T, int d, int N,
                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
-  using Tp = typename E::T;
-  const dim3 grid((T + kTokens - 1) / kTokens), block(256);
-  const Tp* up = (const Tp*)u;
-  const Tp* ep = (const Tp*)Eg;
-  if (N <= 16)
-    router_kernel<E, 1><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  else if (N <= 32)
-    router_kernel<E, 2><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  else if (N <= 64)
-    router_kernel<E, 4><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  else if (N <= 128)
-    router_kernel<E, 8><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  else
-    router_kernel<E, 16><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  return hipGetLastError();
+  if (N <= 16) return launch_router_f<E, 1>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
+  if (N <= 32) return launch_router_f<E, 2>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
+  if (N <= 64) return launch_router_f<E, 4>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
+  if (N <= 128) return launch_router_f<E, 8>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
+  return launch_router_f<E, 16>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
 }
 
 }  // namespace
