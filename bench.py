@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--decode-workload", default="moe16b_decode_bf16")
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--profile-mode", action="store_true",
                     help="for hardware-counter runs: a 1 GiB device copy (calibration) and two "
                          "layer forwards of the workload, nothing else")
