@@ -56,8 +56,10 @@ __device__ __forceinline__ int xcd_swizzle(int b, int G) {
 __global__ __launch_bounds__(64) void tile_table_kernel(const int32_t* __restrict__ offsets,
                                                         int N, int K_s, int T, int TK, int bm1,
                                                         int bm2, int32_t* __restrict__ tiles1,
-                                                        int32_t* __restrict__ tiles2) {
+                                                        int32_t* __restrict__ tiles2,
+                                                        int32_t* __restrict__ counters) {
   const int lane = threadIdx.x;
+  if (lane < 16) counters[lane] = 0;  // the persistent GEMMs' tile claims
   for (int which = 0; which < 2; ++which) {
     const int V = which == 0 ? N + K_s : N + (K_s > 0 ? 1 : 0);
     const int bm = which == 0 ? bm1 : bm2;
@@ -714,6 +716,7 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   __shared__ int s_tab[kMaxV + 1];
   __shared__ int s_dst[kPipeBM];
   __shared__ __attribute__((aligned(16))) float s_gate[kPipeBM];
+  __shared__ int s_claim;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -726,7 +729,10 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   // round-robin over the XCDs) walk that XCD's contiguous range of tiles, so
   // concurrent tiles share an expert's weights and tokens in the XCD's L2.
   // The ranges split the work, not the tile count: a GEMM2 tile of the shared
-  // experts contracts over K_s * I and costs K_s routed tiles.
+  // experts contracts over K_s * I and costs K_s routed tiles.  Inside a
+  // range, each block takes one tile by its index and then claims the next
+  // unprocessed one from the range's counter, so blocks that drew cheap
+  // tiles (an expert's last, partly filled m-tile) take more of them.
   const int V = load_tile_table<MODE>(a, s_tab);
   const int nt = (MODE == 1 ? a.I : a.d) / BNO;
   const int total = s_tab[V] * nt;
@@ -743,6 +749,7 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   const int start = first_at(Wt * x / X), end = first_at(Wt * (x + 1) / X);
   int L = start + lb;
   if (L >= end) return;
+  int* const claims = a.counters + (MODE - 1) * 8 + x;
 
   Tile ti = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, L));
   PipeLoads<NINST> ld;
@@ -758,8 +765,14 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
     // out of AGPRs, so every wavefront multiplies (the padded rows repeat
     // the expert's last slot and are never stored).
     const bool active = W == 4 || ti.m0 + wm * FM * 32 < ti.rows;
-    const int Ln = L + nbx;
-    const bool has_next = Ln < end;
+    // The block's next tile, needed at the last k-step, is claimed at the end
+    // of the first k-step: the wait for the counter's reply then coincides
+    // with the wait for that k-step's loads (with only two k-steps it is
+    // claimed at once).
+    int claim = 0;
+    if (nsteps == 2 && tid == 0) claim = atomicAdd(claims, 1);
+    int Ln = end;
+    bool has_next = false;
     // destination row and gate of tile row `tid`, kept in registers until the epilogue
     int my_dst = -1;
     float my_gate = 1.f;
@@ -775,13 +788,19 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
 
     Tile tn = ti;
     for (int s = 0; s < nsteps; s += 2) {
+      if (s + 2 >= nsteps && tid == 0) s_claim = start + nbx + claim;
       // even k-step: slot 0 holds k-step s; k-step s + 1 goes to slot 1
       pipe_sync();
       pipe_mma<E, MODE, FM>(lds0, wm, wn, lane, acc, active,
                             pipe_dma_base<E, MODE>(a, ti, ld, s + 1, is_a), ld.off,
                             lds1 + wave * NINST * 1024);
+      if (s == 0 && nsteps > 2 && tid == 0) claim = atomicAdd(claims, 1);
       // odd k-step: slot 1 holds k-step s + 1; slot 0 gets k-step s + 2, or
       // the next tile's first k-step after the last one
+      if (s + 2 >= nsteps) {
+        Ln = uni(s_claim);
+        has_next = Ln < end;
+      }
       if (s + 2 >= nsteps && has_next) {
         tn = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, Ln));
         pipe_prepare<E, MODE>(a, tn, wave, lane, ld);  // this tile's loads are all issued
@@ -1144,13 +1163,13 @@ hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int expert_tile_table_ints(int N, int K_s) { return (N + K_s + 1) + (N + 2); }
+int expert_tile_table_ints(int N, int K_s) { return (N + K_s + 1) + (N + 2) + 16; }
 
 hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream) {
   const int es = dtype == 1 ? 2 : 4;
   tile_table_kernel<<<1, 64, 0, stream>>>(a.offsets, a.N, a.K_s, a.T, a.T * a.K,
                                           shape1(a, es).bm(), shape2(a, es).bm(), a.tiles1,
-                                          a.tiles2);
+                                          a.tiles2, a.counters);
   return hipGetLastError();
 }
 

@@ -270,6 +270,7 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
   a.Y_shared = ws + L.Y_shared;
   a.tiles1 = (int32_t*)(ws + L.tiles);
   a.tiles2 = a.tiles1 + (N + K_s + 1);
+  a.counters = a.tiles2 + (N + 2);
   a.T = T;
   a.d = d;
   a.I = I;
@@ -382,6 +383,7 @@ moe_status_t moe_expert_ffn(const void* u, const void* W_routed, const void* W_s
   a.Y_shared = Y_shared;
   a.tiles1 = (int32_t*)workspace;
   a.tiles2 = a.tiles1 + (N + K_s + 1);
+  a.counters = a.tiles2 + (N + 2);
   a.T = T;
   a.d = d;
   a.I = I;

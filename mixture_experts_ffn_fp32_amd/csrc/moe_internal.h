@@ -97,6 +97,7 @@ struct ExpertArgs {
   void* Y_shared;              // [T][d]
   int32_t* tiles1;             // [N+K_s+1] m-tile prefix for GEMM1
   int32_t* tiles2;             // [N+2]     m-tile prefix for GEMM2
+  int32_t* counters;           // [16]      tile claims per XCD (GEMM1, GEMM2), zeroed per launch
   int T, d, I, N, K, K_s;
 };
 int expert_tile_table_ints(int N, int K_s);
