@@ -37,6 +37,10 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--sweep", action="store_true",
+                    help="granularity sweep instead of the benchmark line: the same layer "
+                         "cut into m in {1,2,4,8} times finer experts, K_s in {0,1} shared, at "
+                         "equal parameters and FLOPs; prints one JSON line per configuration")
     ap.add_argument("--profile-mode", action="store_true",
                     help="for hardware-counter runs: a 1 GiB device copy (calibration) and two "
                          "layer forwards of the workload, nothing else")
@@ -139,6 +143,44 @@ def cpu_baseline(inp, n_tokens):
                       f"all experts' weights decoded), {dt:.2f} s wall"}
 
 
+def sweep(args):
+    """Granularity sweep (equal expert parameters and FLOPs per token): one JSON line per
+    configuration.  Inputs are drawn on the GPU (torch's seeded generator: u ~ N(0,1),
+    gate vectors and weights ~ N(0, sigma^2), bf16); their values only set the routing,
+    which is near-uniform as in the main workload."""
+    import torch
+
+    import moe_inputs
+    import mixture_experts_ffn_fp32_amd as mx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mx.load_library()
+    for m, ks in moe_inputs.GRANULARITY_SWEEP:
+        w = moe_inputs.granularity(m, ks)
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed)
+        bf = torch.bfloat16
+        t = {"u": torch.randn(w.T, w.d, generator=g, device=dev, dtype=bf),
+             "E": torch.randn(w.N, w.d, generator=g, device=dev, dtype=bf) * w.sigma,
+             "Wr": torch.randn(w.N * 3 * w.I * w.d, generator=g, device=dev, dtype=bf) * w.sigma,
+             "Ws": (torch.randn(w.K_s * 3 * w.I * w.d, generator=g, device=dev, dtype=bf) * w.sigma
+                    if w.K_s else None),
+             "bias": None}
+        ms, _ = time_layer(mx, t, w, args.steps, args.warmup, False)
+        _, stages = time_layer(mx, t, w, args.steps, 1, True)
+        step = ms / args.steps / 1e3
+        tflops = w.flops_per_token() * w.T / step / 1e12
+        print(json.dumps({
+            "sweep": w.name, "m": m, "shared_experts": ks, "routed_experts": w.N, "top_k": w.K,
+            "intermediate": w.I, "T": w.T, "d": w.d, "dtype": w.dtype,
+            "ms_per_step": round(step * 1e3, 4), "tokens_per_s": round(w.T / step, 1),
+            "layer_tflops": round(tflops, 2), "layer_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items()}}), flush=True)
+        del t
+        torch.cuda.empty_cache()
+
+
 def traffic_record(kernel_src: str, key: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source (else None)."""
@@ -162,6 +204,8 @@ def main():
         sys.exit(2)
     if args.profile_mode:
         return profile_mode(args)
+    if args.sweep:
+        return sweep(args)
     import torch
 
     import moe_inputs

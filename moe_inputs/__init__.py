@@ -195,3 +195,21 @@ def custom(T, d, N, K, K_s, I, dtype="f32", sigma=0.02, seed=7, zipf_s=None, nam
 
 __all__ = ["Workload", "WORKLOADS", "MoEInputs", "make", "custom",
            "f32_to_bf16_bits", "bf16_bits_to_f32"]
+
+
+# Granularity sweep at equal parameters and equal compute (DeepSeekMoE paper
+# summary, papercache.org, sec. 3.1 fine-grained expert segmentation and
+# sec. 3.2 shared expert isolation, Fig. 2): a conventional layer of N0
+# experts of intermediate size I0 with top-K0 routing is cut into m * N0
+# experts of size I0 / m with top m * K0; K_s of those experts then become
+# shared, leaving m * N0 - K_s routed experts with top m * K0 - K_s.  m = 1,
+# K_s = 0 is the conventional top-2 layer.
+GRANULARITY_SWEEP = [(1, 0), (1, 1), (2, 0), (2, 1), (4, 0), (4, 1), (8, 0), (8, 1)]
+
+
+def granularity(m: int, K_s: int, T: int = 8192, d: int = 2048, N0: int = 16, K0: int = 2,
+                I0: int = 5632, dtype: str = "bf16", sigma: float = 0.02, seed: int = 110) -> Workload:
+    if I0 % m != 0:
+        raise ValueError("I0 must split into m equal parts")
+    return Workload(f"gran_m{m}_ks{K_s}", T=T, d=d, N=m * N0 - K_s, K=m * K0 - K_s, K_s=K_s,
+                    I=I0 // m, dtype=dtype, sigma=sigma, seed=seed + 10 * m + K_s)

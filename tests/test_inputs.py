@@ -55,3 +55,18 @@ def test_zipf_bias_profile():
     ranks = np.rint(r).astype(int)
     np.testing.assert_allclose(p, ranks ** -1.1 / (np.arange(1, 129) ** -1.1).sum(), rtol=1e-5)
     assert moe_inputs.make("moe16b_prefill_bf16", T=1).gate_bias() is None
+
+
+def test_granularity_sweep_keeps_parameters_and_compute():
+    """Every point of the sweep has the conventional layer's expert parameters and
+    per-token expert FLOPs ([DSMoE] sec. 3.1/3.2, Fig. 2: both stay unchanged)."""
+    base = moe_inputs.granularity(1, 0)
+    assert (base.N, base.K, base.K_s, base.I) == (16, 2, 0, 5632)
+    params = lambda w: (w.N + w.K_s) * 3 * w.I * w.d           # noqa: E731
+    expert_flops = lambda w: 6 * w.d * w.I * (w.K + w.K_s)     # noqa: E731
+    for m, ks in moe_inputs.GRANULARITY_SWEEP:
+        w = moe_inputs.granularity(m, ks)
+        assert params(w) == params(base), (m, ks)
+        assert expert_flops(w) == expert_flops(base), (m, ks)
+        assert w.N + w.K_s == 16 * m and w.K + w.K_s == 2 * m
+        assert w.I % 64 == 0
