@@ -148,7 +148,7 @@ __device__ __forceinline__ int load_tile_table(const ExpertArgs& a, int* s_tab) 
 // Tile L of the table in LDS (every thread searches the same entries: no barrier).
 template <int BM, int BNO, int MODE>
 __device__ __forceinline__ Tile tile_of(const ExpertArgs& a, const int* s_tab, int V, int L) {
-  const int nt = (MODE == 1 ? a.I : a.d) / BNO;
+  const int nt = ((MODE == 1 ? a.I : a.d) + BNO - 1) / BNO;  // the last n-tile may be partial
   int lo = 0, hi = V - 1;  // largest v with s_tab[v] * nt <= L
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -198,10 +198,11 @@ __device__ __forceinline__ const typename E::T* tile_row_ptr(const ExpertArgs& a
   const int rb = r - BM;
   const Tp* W = ti.routed ? (const Tp*)a.W_routed + (size_t)ti.v * 3 * Id
                           : (const Tp*)a.W_shared + (size_t)(MODE == 1 ? ti.v - a.N : 0) * 3 * Id;
+  // columns past the last one (a partial last n-tile) reread the last row
   if (MODE == 1)
-    return rb < BNB / 2 ? W + (size_t)(ti.n0 + rb) * a.d
-                        : W + Id + (size_t)(ti.n0 + rb - BNB / 2) * a.d;
-  return W + 2 * Id + (size_t)(ti.n0 + rb) * a.I;
+    return rb < BNB / 2 ? W + (size_t)min(ti.n0 + rb, a.I - 1) * a.d
+                        : W + Id + (size_t)min(ti.n0 + rb - BNB / 2, a.I - 1) * a.d;
+  return W + 2 * Id + (size_t)min(ti.n0 + rb, a.d - 1) * a.I;
 }
 
 // Element offset of contraction index k0 in a B row.  The shared experts'
@@ -248,6 +249,7 @@ __device__ __forceinline__ void store_tile(const ExpertArgs& a, const Tile& ti, 
           const float gt = acc[fm][fn][r], up = acc[fm][fn + FN / 2][r];
           const float hv = gt / (1.f + expf(-gt)) * up;   // SiLU(gate) * up
           const int col = ti.n0 + (wn * (FN / 2) + fn) * 32 + lc;
+          if (col >= a.I) continue;  // partial last n-tile
           Tp* dst = ti.routed
                         ? (Tp*)a.H_routed + (size_t)(ti.row_base + p) * a.I + col
                         : (Tp*)a.H_shared + (size_t)p * a.K_s * a.I + (size_t)(ti.v - a.N) * a.I + col;
@@ -267,7 +269,7 @@ __device__ __forceinline__ void store_tile(const ExpertArgs& a, const Tile& ti, 
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           const int col = ti.n0 + (wn * FN + fn) * 32 + lc;
-          store_from_f32<E>(dst + col, acc[fm][fn][r] * g);
+          if (col < a.d) store_from_f32<E>(dst + col, acc[fm][fn][r] * g);
         }
       }
     }
@@ -369,10 +371,12 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
 // direct-to-LDS load as a possible LDS access of unknown order and then
 // waits for every outstanding LDS read (lgkmcnt(0)) before each MFMA that
 // needs one; buffer loads keep its partial lgkmcnt waits exact.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* __restrict__ wr) {
+// `nrec` bounds the offsets (bytes): 0 makes the load return zeros.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* __restrict__ wr,
+                                      int nrec = 0x7fffffff) {
 #if MOE_DMA_BUFFER
   const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wr, 16, off,
                                            0, 0, 0);
 #else
@@ -510,11 +514,12 @@ template <class E, int MODE, int FM, int NI>
 __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm, int wn, int lane,
                                          f32x16 (&acc)[FM][4], bool active,
                                          const uint8_t* db, const uint32_t (&off)[NI],
-                                         uint8_t* __restrict__ wr) {
+                                         uint8_t* __restrict__ wr, int nrec = 0x7fffffff) {
   constexpr int FN = 4, KG = kPipeRB / 32, PARTS = MOE_DMA_GROUPS, PER = NI / PARTS;
   static_assert(NI % PARTS == 0 && PARTS <= KG, "DMA parts");
   if (!active) {
-    dma_fill<NI>(wr, db, off);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(db, off[i], wr + i * 1024, nrec);
     return;
   }
   u32x4 af[2][FM], bfr[2][FN];
@@ -523,7 +528,7 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm,
   for (int kg = 0; kg < KG; ++kg) {
     if (kg < PARTS) {
 #pragma unroll
-      for (int i = kg * PER; i < (kg + 1) * PER; ++i) dma16(db, off[i], wr + i * 1024);
+      for (int i = kg * PER; i < (kg + 1) * PER; ++i) dma16(db, off[i], wr + i * 1024, nrec);
     }
     if (kg + 1 < KG)
       load_frags<FM, FN, kPipeRB, kPipeBM, kPipeBNB, MODE>(rd, kg + 1, wm, wn, lane,
@@ -676,9 +681,10 @@ __device__ __forceinline__ void pipe_store_bf16(const ExpertArgs& a, const Tile&
         drow[k] = s_dst[row];
         v[k] = *(const u32x4*)(stage + row * (COLS * 2) + ((c ^ (row & 15)) << 4));
       }
+      const bool col_ok = ti.n0 + (MODE == 1 ? 0 : pass * COLS) + c * 8 < (MODE == 1 ? a.I : a.d);
 #pragma unroll
       for (int k = 0; k < NB; ++k)
-        if (drow[k] >= 0) *(u32x4*)(base + (size_t)drow[k] * pitch + c * 8) = v[k];
+        if (drow[k] >= 0 && col_ok) *(u32x4*)(base + (size_t)drow[k] * pitch + c * 8) = v[k];
     }
     lds_sync();
   }
@@ -734,7 +740,7 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   // unprocessed one from the range's counter, so blocks that drew cheap
   // tiles (an expert's last, partly filled m-tile) take more of them.
   const int V = load_tile_table<MODE>(a, s_tab);
-  const int nt = (MODE == 1 ? a.I : a.d) / BNO;
+  const int nt = ((MODE == 1 ? a.I : a.d) + BNO - 1) / BNO;
   const int total = s_tab[V] * nt;
   const int Lr = MODE == 2 ? s_tab[a.N] * nt : total;  // tiles before the shared ones
   const int w = MODE == 2 ? max(a.K_s, 1) : 1;
@@ -758,7 +764,10 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
 
   while (true) {
     const int Kc = MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I);
-    const int nsteps = Kc / kStep;  // even (the host only picks this kernel then)
+    // an odd k-step count is padded with one k-step of zeros (loaded as out
+    // of range), so that k-steps always come in (slot 0, slot 1) pairs
+    const int nreal = Kc / kStep;
+    const int nsteps = nreal + (nreal & 1);
     // A wavefront whose rows all lie past the expert's last slot skips its
     // MFMAs when it shares a SIMD (W = 8); with one wavefront per SIMD (W = 4)
     // skipping saves no time, and the branch would force the accumulators
@@ -792,8 +801,8 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
       // even k-step: slot 0 holds k-step s; k-step s + 1 goes to slot 1
       pipe_sync();
       pipe_mma<E, MODE, FM>(lds0, wm, wn, lane, acc, active,
-                            pipe_dma_base<E, MODE>(a, ti, ld, s + 1, is_a), ld.off,
-                            lds1 + wave * NINST * 1024);
+                            pipe_dma_base<E, MODE>(a, ti, ld, s + 1 < nreal ? s + 1 : 0, is_a),
+                            ld.off, lds1 + wave * NINST * 1024, s + 1 < nreal ? 0x7fffffff : 0);
       if (s == 0 && nsteps > 2 && tid == 0) claim = atomicAdd(claims, 1);
       // odd k-step: slot 1 holds k-step s + 1; slot 0 gets k-step s + 2, or
       // the next tile's first k-step after the last one
@@ -1068,10 +1077,11 @@ int pipe_waves() {
   return v;
 }
 
-// The pipelined kernel needs 128-column H tiles (I % 128), 256-column Y tiles
-// (d % 256) and an even number of 128-byte k-steps in every contraction.
-bool pipe_ok1(const ExpertArgs& a, int es) { return a.I % 128 == 0 && (a.d * es) % 256 == 0; }
-bool pipe_ok2(const ExpertArgs& a, int es) { return a.d % 256 == 0 && (a.I * es) % 256 == 0; }
+// The pipelined kernel takes any shape the ABI admits (d and I multiples of
+// 64: whole 128-byte k-steps; an odd k-step count gets one zero-filled
+// k-step; partial last n-tiles are masked).
+bool pipe_ok1(const ExpertArgs& a, int es) { return (a.d * es) % 128 == 0 && a.I % 64 == 0; }
+bool pipe_ok2(const ExpertArgs& a, int es) { return (a.I * es) % 128 == 0 && a.d % 64 == 0; }
 
 Shape shape1(const ExpertArgs& a, int es) {
   if (small_m(a) && es == 2 && !force_reg()) return Shape{2, 0, 0, 0, 0};
@@ -1121,7 +1131,7 @@ int cu_count() {
 template <class E, int MODE, int W>
 hipError_t launch_pipe(const ExpertArgs& a, hipStream_t st) {
   constexpr int BNO = MODE == 1 ? kPipeBNB / 2 : kPipeBNB;
-  long long g = grid_tiles(a, kPipeBM, (MODE == 1 ? a.I : a.d) / BNO, MODE);
+  long long g = grid_tiles(a, kPipeBM, ((MODE == 1 ? a.I : a.d) + BNO - 1) / BNO, MODE);
   if (g <= 0) return hipSuccess;
   g = std::min<long long>(g, (long long)cu_count());  // persistent: one block per CU
   expert_gemm_pipe_kernel<E, MODE, W><<<dim3((unsigned)g), dim3(PipeCfg<W>::kThreads), 0, st>>>(a);
