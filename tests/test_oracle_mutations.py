@@ -52,3 +52,37 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                         str(tmp_path / "tests" / "test_oracle_pins.py")],
                        cwd=tmp_path, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"planted mistake {name!r} passed every pin:\n{r.stdout[-2000:]}"
+
+
+# Planted mistakes in the backward oracle; tests/test_oracle_backward.py must catch each.
+BACKWARD_MUTATIONS = {
+    "silu_grad_is_sigmoid": ('return sig * (1.0 + a * (1.0 - sig))', 'return sig'),
+    "routed_dy_without_gate": ('y, dx, dWg, dWu, dWd = swiglu_ffn_backward(u[rows], *Wi, gi * dh[rows])',
+                               'y, dx, dWg, dWu, dWd = swiglu_ffn_backward(u[rows], *Wi, dh[rows])'),
+    "softmax_backward_no_centering": ('dz = s * (ds - np.sum(s * ds, axis=1, keepdims=True))',
+                                      'dz = s * ds'),
+    "no_residual_gradient": ('du = dh.copy()                                     # residual',
+                             'du = np.zeros_like(dh)'),
+    "dc_uses_silu_grad": ('dc = dp * silu(a)', 'dc = dp * silu_grad(a)'),
+    "gate_scales_ds": ('ds[rows, i] = np.sum(dh[rows] * y, axis=1)',
+                       'ds[rows, i] = np.sum(gi * dh[rows] * y, axis=1)'),
+    "router_gradient_dropped": ('du += dz @ _f64(E_gate)', 'pass'),
+    "gate_and_up_swapped": ('dx = da @ Wg + dc @ Wu', 'dx = da @ Wu + dc @ Wg'),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTATIONS))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    before, after = BACKWARD_MUTATIONS[name]
+    src = open(os.path.join(ROOT, "oracle", "moe_backward.py")).read()
+    assert before in src, "mutation anchor no longer present in the backward oracle"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    shutil.copytree(os.path.join(ROOT, "moe_inputs"), tmp_path / "moe_inputs")
+    (tmp_path / "tests").mkdir()
+    for f in ("test_oracle_backward.py", "conftest.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    (tmp_path / "oracle" / "moe_backward.py").write_text(src.replace(before, after))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        str(tmp_path / "tests" / "test_oracle_backward.py")],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"planted mistake {name!r} passed every pin:\n{r.stdout[-2000:]}"
