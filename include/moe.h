@@ -1,5 +1,5 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward.
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer (forward and backward).
  *
  * The operation (DeepSeekMoE paper summary, papercache.org, sec. 3.2 "Shared
  * Expert Isolation", full layer equation; the conventional top-K layer of
@@ -154,6 +154,46 @@ moe_status_t moe_balance_stats(const float* scores, const int32_t* idx, int T, i
                                const int32_t* group_of, int D, float alpha1, float alpha2,
                                float* f, float* P, float* f_dev, float* P_dev, float* losses,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- layer backward ----
+ * Gradients of the scalar sum_t dh_t . h_t for h = moe_layer_forward(u, ...),
+ * by the chain rule through the sec. 3.2 layer equation (DeepSeekMoE paper
+ * summary, papercache.org; the pages train the layer but print no backward
+ * formulas), with the top-K set of each token held fixed -- the selection is
+ * piecewise constant in the scores, so it contributes no derivative:
+ *   per expert slot (x = u_t, a = W_gate x, c = W_up x, p = SiLU(a) c,
+ *   dy = g dh for a routed slot, dh for a shared one):
+ *     dW_down += dy p^T, dp = W_down^T dy, da = dp c SiLU'(a), dc = dp SiLU(a),
+ *     dW_gate += da x^T, dW_up += dc x^T, du_t += W_gate^T da + W_up^T dc;
+ *   routed gate: ds_{i,t} = dh_t . FFN_i(u_t) for i in the top-K, else 0;
+ *   softmax:     dz_{i,t} = s_{i,t} (ds_{i,t} - sum_j s_{j,t} ds_{j,t});
+ *   router:      du_t += E_gate^T dz_t, dE_gate += dz_t u_t^T, db += dz_t;
+ *   residual:    du_t += dh_t.
+ * The forward's routing is recomputed from u (same kernels, same bits).
+ * Inputs: u, E_gate, W_routed, W_shared, gate_bias as for moe_layer_forward;
+ *   dh [T][d] dtype (upstream gradient).
+ * Outputs (device):
+ *   du         [T][d]             dtype    must not overlap u or dh
+ *   dE_gate    [N][d]             float32
+ *   dgate_bias [N]                float32  may be NULL (then not written;
+ *                                          gate_bias may still be given)
+ *   dW_routed  [N][3*I*d]         float32  in the weights' block layout
+ *   dW_shared  [K_s][3*I*d]       float32  NULL iff K_s == 0
+ * Intermediates (the recomputed pre-activations, dP, P, dY, per-slot dx, the
+ * softmax gradient) are float32, or dtype where they feed a matrix product;
+ * products accumulate in float32.  Experts that no token selects get zero
+ * weight gradients.
+ * T = 0 writes nothing (the gradients of an empty batch are zero).
+ * Workspace: moe_backward_workspace_size() bytes, 256-byte aligned, about
+ * T*K*(6*I + 2*d)*4 + T*K_s*(6*I + d)*4 bytes for float32 (less for bf16). */
+moe_status_t moe_backward_workspace_size(int T, int d, int I, int N, int K, int K_s, int dtype,
+                                         size_t* bytes);
+moe_status_t moe_layer_backward(const void* u, const void* E_gate, const void* W_routed,
+                                const void* W_shared, int N, int K, int K_s, int T, int d, int I,
+                                int dtype, const float* gate_bias, const void* dh, void* du,
+                                float* dE_gate, float* dgate_bias, float* dW_routed,
+                                float* dW_shared, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* ---- per-stage timing (for profiling; off by default) ----
  * When enabled, moe_layer_forward records a HIP event pair around each of its

@@ -1,6 +1,7 @@
 // C ABI of the DeepSeekMoE layer forward: argument validation, workspace
 // layout and the stream-ordered launch sequence.  No device memory is
 // allocated here and nothing waits on the device (except moe_timing_read).
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -410,6 +411,155 @@ moe_status_t moe_combine(const void* u, const void* Y, const void* Y_shared, int
   StageScope sc(6, (hipStream_t)stream);
   hipError_t e = moe::launch_combine(dtype, u, Y, Y_shared, T, d, K, K_s, h, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------- backward
+namespace {
+
+struct BwdLayout {
+  size_t idx, gate, scores, rank, tile_counts, tile_base, counts, offsets, sorted_pair;
+  size_t AC, ACs, dP, dPs, dAC, dACs, P, Ps, dY, dX, dXs, dzE, dz, dE_part, ds_pair, slot_of,
+      db_part, tab, total;
+};
+
+int pad8(int n) { return (n + 7) & ~7; }
+
+BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype) {
+  BwdLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  const size_t TK = (size_t)T * K, es = elem_size(dtype), nt = (size_t)rank_tiles(T);
+  L.idx = take(TK * 4);
+  L.gate = take(TK * 4);
+  L.scores = take((size_t)T * N * 4);
+  L.rank = take(TK * 4);
+  L.tile_counts = take(nt * N * 4);
+  L.tile_base = take(nt * N * 4);
+  L.counts = take((size_t)N * 4);
+  L.offsets = take((size_t)(N + 1) * 4);
+  L.sorted_pair = take(TK * 4);
+  L.AC = take(TK * 2 * I * 4);
+  L.ACs = take((size_t)T * K_s * 2 * I * 4);
+  L.dP = take(TK * I * 4);
+  L.dPs = take((size_t)T * K_s * I * 4);
+  L.dAC = take(TK * 2 * I * es);
+  L.dACs = take((size_t)T * K_s * 2 * I * es);
+  L.P = take(TK * I * es);
+  L.Ps = take((size_t)T * K_s * I * es);
+  L.dY = take(TK * d * es);
+  L.dX = take(TK * d * 4);
+  L.dXs = take((size_t)K_s * T * d * 4);
+  L.dzE = take((size_t)T * pad8(N) * es);
+  L.dz = take((size_t)T * N * 4);
+  L.dE_part = take((size_t)moe::backward_de_chunks(T) * N * d * 4);
+  L.ds_pair = take(TK * 4);
+  L.slot_of = take(TK * 4);
+  L.db_part = take((size_t)moe::backward_db_blocks(T) * N * 8);
+  L.tab = take((size_t)(std::max(N + K_s, moe::backward_de_chunks(T)) + 1) * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+moe_status_t moe_backward_workspace_size(int T, int d, int I, int N, int K, int K_s, int dtype,
+                                         size_t* bytes) {
+  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  if (s != MOE_OK) return s;
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = T == 0 ? 0 : make_bwd_layout(T, d, I, N, K, K_s, dtype).total;
+  return ok();
+}
+
+moe_status_t moe_layer_backward(const void* u, const void* E_gate, const void* W_routed,
+                                const void* W_shared, int N, int K, int K_s, int T, int d, int I,
+                                int dtype, const float* gate_bias, const void* dh, void* du,
+                                float* dE_gate, float* dgate_bias, float* dW_routed,
+                                float* dW_shared, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  if ((s = check_ptr("u", u, true)) != MOE_OK) return s;
+  if ((s = check_ptr("E_gate", E_gate, true)) != MOE_OK) return s;
+  if ((s = check_ptr("W_routed", W_routed, true)) != MOE_OK) return s;
+  if ((s = check_ptr("W_shared", W_shared, K_s > 0)) != MOE_OK) return s;
+  if ((s = check_ptr("gate_bias", gate_bias, false)) != MOE_OK) return s;
+  if ((s = check_ptr("dh", dh, true)) != MOE_OK) return s;
+  if ((s = check_ptr("du", du, true)) != MOE_OK) return s;
+  if ((s = check_ptr("dE_gate", dE_gate, true)) != MOE_OK) return s;
+  if ((s = check_ptr("dgate_bias", dgate_bias, false)) != MOE_OK) return s;
+  if ((s = check_ptr("dW_routed", dW_routed, true)) != MOE_OK) return s;
+  if ((s = check_ptr("dW_shared", dW_shared, K_s > 0)) != MOE_OK) return s;
+  if ((s = check_ptr("workspace", workspace, true)) != MOE_OK) return s;
+  const size_t act = (size_t)T * d * elem_size(dtype);
+  if (overlap(du, act, u, act)) return fail(MOE_ERR_INVALID_ARG, "du overlaps u");
+  if (overlap(du, act, dh, act)) return fail(MOE_ERR_INVALID_ARG, "du overlaps dh");
+  const BwdLayout L = make_bwd_layout(T, d, I, N, K, K_s, dtype);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_backward_workspace_size()");
+  if (overlap(du, act, workspace, L.total))
+    return fail(MOE_ERR_INVALID_ARG, "du overlaps workspace");
+  const size_t wr = (size_t)N * 3 * I * d * 4;
+  if (overlap(dW_routed, wr, workspace, L.total))
+    return fail(MOE_ERR_INVALID_ARG, "dW_routed overlaps workspace");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* idx = (int32_t*)(ws + L.idx);
+  float* gate = (float*)(ws + L.gate);
+  float* scores = (float*)(ws + L.scores);
+  hipError_t e;
+  if ((e = moe::launch_router(dtype, u, E_gate, gate_bias, T, d, N, K, idx, gate, scores, st)) !=
+      hipSuccess)
+    return hip_fail(e, "router launch");
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* sorted_pair = (int32_t*)(ws + L.sorted_pair);
+  if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
+                        (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
+                        (int32_t*)(ws + L.tile_base), st)) != MOE_OK)
+    return s;
+  moe::BwdArgs a{};
+  a.u = u;
+  a.dh = dh;
+  a.E_gate = E_gate;
+  a.W_routed = W_routed;
+  a.W_shared = W_shared;
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.AC = (float*)(ws + L.AC);
+  a.ACs = (float*)(ws + L.ACs);
+  a.dP = (float*)(ws + L.dP);
+  a.dPs = (float*)(ws + L.dPs);
+  a.dAC = ws + L.dAC;
+  a.dACs = ws + L.dACs;
+  a.P = ws + L.P;
+  a.Ps = ws + L.Ps;
+  a.dY = ws + L.dY;
+  a.dX = (float*)(ws + L.dX);
+  a.dXs = (float*)(ws + L.dXs);
+  a.dzE = ws + L.dzE;
+  a.dE_part = (float*)(ws + L.dE_part);
+  a.dE_gate = dE_gate;
+  a.dW_routed = dW_routed;
+  a.dW_shared = dW_shared;
+  a.T = T;
+  a.d = d;
+  a.I = I;
+  a.N = N;
+  a.K = K;
+  a.K_s = K_s;
+  a.NP = pad8(N);
+  if ((e = moe::launch_backward(dtype, a, gate, scores, idx, (float*)(ws + L.ds_pair),
+                                (int32_t*)(ws + L.slot_of), (float*)(ws + L.dz),
+                                (double*)(ws + L.db_part), dgate_bias, du,
+                                (int32_t*)(ws + L.tab), st)) != hipSuccess)
+    return hip_fail(e, "backward launch");
   return ok();
 }
 

@@ -118,6 +118,41 @@ hipError_t launch_balance(const float* scores, const int32_t* idx, int T, int N,
                           float* P, float* f_dev, float* P_dev, float* losses, void* workspace,
                           hipStream_t stream);
 
+// Backward pass (csrc/backward.hip).  Slot-ordered buffers follow the
+// dispatch order of the forward (routed slots), shared ones are per token.
+struct BwdArgs {
+  const void* u;
+  const void* dh;
+  const void* E_gate;
+  const void* W_routed;
+  const void* W_shared;
+  const int32_t* offsets;      // [N+1]
+  const int32_t* sorted_pair;  // [T*K]
+  float* AC;                   // [T*K][2I]      a = W_gate x, c = W_up x (routed slots)
+  float* ACs;                  // [T][K_s*2I]    the same for the shared experts
+  float* dP;                   // [T*K][I]       W_down^T dh (routed slots)
+  float* dPs;                  // [T][K_s*I]
+  void* dAC;                   // [T*K][2I] dtype  [da, dc]
+  void* dACs;                  // [T][K_s*2I]
+  void* P;                     // [T*K][I] dtype   p = SiLU(a) c
+  void* Ps;                    // [T][K_s*I]
+  void* dY;                    // [T*K][d] dtype   g * dh rows
+  float* dX;                   // [T*K][d]       W_gate^T da + W_up^T dc (routed slots)
+  float* dXs;                  // [K_s][T][d]
+  void* dzE;                   // [T][NP] dtype  softmax gradient, rows padded to NP
+  float* dE_part;              // [chunks][N][d] partial router gradients
+  float* dE_gate;              // [N][d]
+  float* dW_routed;            // N weight blocks (float32)
+  float* dW_shared;            // K_s weight blocks (float32)
+  int T, d, I, N, K, K_s, NP;
+};
+int backward_db_blocks(int T);
+int backward_de_chunks(int T);
+hipError_t launch_backward(int dtype, const BwdArgs& a, const float* gate, const float* scores,
+                           const int32_t* idx, float* ds_pair, int32_t* slot_of, float* dz,
+                           double* db_part, float* dgate_bias, void* du, int32_t* tab,
+                           hipStream_t stream);
+
 hipError_t launch_combine(int dtype, const void* u, const void* Y, const void* Y_shared, int T,
                           int d, int K, int K_s, void* h, hipStream_t stream);
 

@@ -23,7 +23,8 @@ _DTYPES = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}
 EXPORTED = ("moe_last_error", "moe_workspace_size", "moe_layer_forward", "moe_route",
             "moe_dispatch_workspace_size", "moe_dispatch", "moe_expert_ffn_workspace_size",
             "moe_expert_ffn", "moe_combine", "moe_balance_workspace_size", "moe_balance_stats",
-            "moe_timing_enable", "moe_timing_read")
+            "moe_backward_workspace_size", "moe_layer_backward", "moe_timing_enable",
+            "moe_timing_read")
 
 
 class MoEError(RuntimeError):
@@ -60,6 +61,9 @@ def load_library(path: str = LIB_PATH):
         "moe_balance_workspace_size": [i, i, szp],
         "moe_balance_stats": [vp, vp, i, i, i, vp, i, ctypes.c_float, ctypes.c_float, vp, vp, vp,
                               vp, vp, vp, sz, vp],
+        "moe_backward_workspace_size": [i, i, i, i, i, i, i, szp],
+        "moe_layer_backward": [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp,
+                               sz, vp],
         "moe_timing_enable": [i],
         "moe_timing_read": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)],
     }
@@ -135,6 +139,46 @@ def layer_forward(u, E_gate, W_routed, W_shared, N: int, K: int, K_s: int, gate_
                                dt, _p(gate_bias), _p(h), _p(workspace),
                                workspace.numel() * workspace.element_size(), _stream()))
     return h
+
+
+def backward_workspace_size(T, d, I, N, K, K_s, dtype_code) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().moe_backward_workspace_size(T, d, I, N, K, K_s, dtype_code,
+                                                      ctypes.byref(out)))
+    return out.value
+
+
+def layer_backward(u, E_gate, W_routed, W_shared, N: int, K: int, K_s: int, dh, gate_bias=None,
+                   workspace=None):
+    """Gradients of sum(dh * h) for h = layer_forward(u, ...); see include/moe.h.
+
+    Returns (du, dE_gate, dgate_bias, dW_routed, dW_shared or None); every gradient
+    but du is float32, the weight gradients in the layout of their weights.  The
+    bias gradient is the same whether or not a bias is given.
+    """
+    L = load_library()
+    T, d = u.shape
+    dt = _dtype_code(u)
+    _dev(u, E_gate, W_routed, W_shared, dh, dtype=u.dtype)
+    _dev(gate_bias, dtype=torch.float32)
+    I = _infer_I(W_routed, N, d)
+    dev = u.device
+    # an empty batch writes nothing: its weight gradients are zeros
+    alloc = torch.zeros if T == 0 else torch.empty
+    du = torch.empty_like(u)
+    dE = alloc(E_gate.shape, dtype=torch.float32, device=dev)
+    db = alloc(N, dtype=torch.float32, device=dev)
+    dWr = alloc(W_routed.shape, dtype=torch.float32, device=dev)
+    dWs = None if K_s == 0 else alloc(W_shared.shape, dtype=torch.float32, device=dev)
+    need = backward_workspace_size(T, d, I, N, K, K_s, dt)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace)
+    _check(L.moe_layer_backward(_p(u), _p(E_gate), _p(W_routed), _p(W_shared), N, K, K_s, T, d, I,
+                                dt, _p(gate_bias), _p(dh), _p(du), _p(dE), _p(db), _p(dWr),
+                                _p(dWs), _p(workspace),
+                                workspace.numel() * workspace.element_size(), _stream()))
+    return du, dE, db, dWr, dWs
 
 
 def route(u, E_gate, K: int, gate_bias=None, want_scores: bool = False):

@@ -29,7 +29,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TENSOR_U, TENSOR_E, TENSOR_ROUTED, TENSOR_SHARED, TENSOR_BIASPERM = 0, 1, 2, 3, 4
+TENSOR_U, TENSOR_E, TENSOR_ROUTED, TENSOR_SHARED, TENSOR_BIASPERM, TENSOR_DH = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -150,6 +150,13 @@ class MoEInputs:
             out[j] = self.shared_block_raw(j)
         return out
 
+    def dh_raw(self) -> np.ndarray:
+        """Upstream gradient of the layer output for the backward pass, [T][d], N(0, 1)."""
+        w = self.w
+        if "dh" not in self._cache:
+            self._cache["dh"] = _draw(w.seed, TENSOR_DH, 0, w.T * w.d, 1.0, w.dtype).reshape(w.T, w.d)
+        return self._cache["dh"]
+
     def gate_bias(self) -> np.ndarray | None:
         """Per-expert logit bias (float32) for skewed workloads, else None."""
         w = self.w
@@ -167,6 +174,9 @@ class MoEInputs:
 
     def E_gate_f32(self) -> np.ndarray:
         return self._to_f32(self.E_gate_raw())
+
+    def dh_f32(self) -> np.ndarray:
+        return self._to_f32(self.dh_raw())
 
     def split_block(self, block: np.ndarray):
         """(W_gate [I][d], W_up [I][d], W_down [d][I]) views of one expert block."""

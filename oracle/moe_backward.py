@@ -83,18 +83,24 @@ def _expert(weights, i):
     return weights(i) if callable(weights) else weights[i]
 
 
-def moe_layer_backward(u, E_gate, routed, shared, N: int, K: int, K_s: int, dh, gate_bias=None):
+def moe_layer_backward(u, E_gate, routed, shared, N: int, K: int, K_s: int, dh, gate_bias=None,
+                       replace_sets=None):
     """All gradients of sum(dh * h) for the layer; the chain rule in the order of the
     formula (residual, shared experts, routed experts, softmax, router).
 
+    replace_sets: optional {t: (idx [K], g [K])} of tokens whose held-fixed set is
+    another admissible one (near_tie_alternatives) instead of the top-K of s.
+
     Returns a dict: du [T][d], dE_gate [N][d], dgate_bias [N], d_routed (list of
     (dW_gate, dW_up, dW_down) per routed expert), d_shared (same per shared expert),
-    and the forward's s, idx, g, ds.
+    and the forward's s, idx, g, ds, dz.
     """
     u, dh = _f64(u), _f64(dh)
     T, d = u.shape
     s = affinity_scores(u, E_gate, gate_bias)
     idx, g, margin = top_k_gates(s, K)
+    for t, (ia, ga) in (replace_sets or {}).items():
+        idx[t], g[t] = ia, ga
     gate = np.zeros((T, N))
     np.put_along_axis(gate, idx, g, axis=1)
 
@@ -123,4 +129,5 @@ def moe_layer_backward(u, E_gate, routed, shared, N: int, K: int, K_s: int, dh, 
     dE = dz.T @ u
     db = dz.sum(axis=0)
     return {"du": du, "dE_gate": dE, "dgate_bias": db, "d_routed": d_routed,
-            "d_shared": d_shared, "s": s, "idx": idx, "g": g, "ds": ds, "margin": margin}
+            "d_shared": d_shared, "s": s, "idx": idx, "g": g, "ds": ds, "dz": dz,
+            "margin": margin}

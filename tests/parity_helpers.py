@@ -129,3 +129,30 @@ def check_h(h_gpu: np.ndarray, h_ref: np.ndarray, u: np.ndarray, tol: float, dty
     assert np.all(err <= tol * delta_scale + rounding), \
         f"{label} MoE delta error {(err - rounding).max():.3e} > {tol} * {delta_scale:.3e}"
     return err.max() / scale
+
+
+# Small workloads (several tiles, ragged tails, degenerate cases) shared by the
+# forward and backward parity tests.
+SMALL = {
+    "ragged_f32": dict(T=300, d=256, N=20, K=5, K_s=2, I=192, dtype="f32"),
+    "ragged_bf16": dict(T=300, d=256, N=20, K=5, K_s=2, I=192, dtype="bf16"),
+    "no_shared_bf16": dict(T=200, d=128, N=8, K=2, K_s=0, I=128, dtype="bf16"),
+    "k_equals_n_f32": dict(T=70, d=64, N=6, K=6, K_s=1, I=64, dtype="f32"),
+    "one_token_bf16": dict(T=1, d=128, N=16, K=4, K_s=1, I=128, dtype="bf16"),
+    "n63_bf16": dict(T=513, d=320, N=63, K=7, K_s=1, I=128, dtype="bf16"),
+    "n256_bf16": dict(T=130, d=128, N=256, K=8, K_s=3, I=64, dtype="bf16"),
+    "n1_f32": dict(T=33, d=64, N=1, K=1, K_s=0, I=64, dtype="f32"),
+    "wide_tokens_bf16": dict(T=2050, d=512, N=16, K=4, K_s=1, I=256, dtype="bf16"),
+    # ends of the granularity sweep (conventional top-2 and 8x finer experts with a
+    # shared one) at a reduced size: I0 = 4096, d = 128
+    "gran_m1_ks0_bf16": dict(T=300, d=128, N=16, K=2, K_s=0, I=4096, dtype="bf16", seed=1101),
+    "gran_m8_ks1_bf16": dict(T=300, d=128, N=127, K=15, K_s=1, I=512, dtype="bf16", seed=1181),
+}
+
+
+def small_inputs(name):
+    kw = dict(SMALL[name])
+    seed = kw.pop("seed", None)
+    if seed is None:
+        seed = 1000 + sorted(k for k in SMALL if "seed" not in SMALL[k]).index(name)
+    return moe_inputs.custom(**kw, sigma=0.08, seed=seed, name=name)

@@ -144,3 +144,45 @@ def test_balance_validation_never_reaches_the_gpu(lib):
     assert _bal(lib, group_of=[0, 0, 1, 1, 3, 3, 3, 3], D=4) == INVALID   # group 2 is empty
     assert "no expert" in lib.moe_last_error().decode()
     assert _bal(lib, group_of=[0] * 8, D=9) == INVALID
+
+
+def _bwd(lib, u=16, E=16, Wr=16, Ws=16, dh=1 << 20, du=1 << 22, dE=1 << 23, db=None,
+         dWr=1 << 24, dWs=1 << 25, ws=1 << 44, wsb=1 << 40, N=64, K=6, K_s=2, T=8, d=2048,
+         I=1408, dt=1, bias=None):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)   # noqa: E731
+    return lib.moe_layer_backward(p(u), p(E), p(Wr), p(Ws), N, K, K_s, T, d, I, dt, p(bias),
+                                  p(dh), p(du), p(dE), p(db), p(dWr), p(dWs), p(ws), wsb, None)
+
+
+def test_backward_validation_never_reaches_the_gpu(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.moe_backward_workspace_size(8, 2048, 1408, 64, 6, 2, 1, ctypes.byref(out)) == OK
+    small = out.value
+    assert lib.moe_backward_workspace_size(64, 2048, 1408, 64, 6, 2, 1, ctypes.byref(out)) == OK
+    assert out.value > small > 0
+    assert lib.moe_backward_workspace_size(0, 2048, 1408, 64, 6, 2, 1, ctypes.byref(out)) == OK
+    assert out.value == 0
+    assert lib.moe_backward_workspace_size(8, 2048, 1400, 64, 6, 2, 1,
+                                           ctypes.byref(out)) == UNSUPPORTED
+    assert _bwd(lib, dh=None) == INVALID
+    assert _bwd(lib, du=None) == INVALID
+    assert _bwd(lib, dE=None) == INVALID
+    assert _bwd(lib, dWr=None) == INVALID
+    assert _bwd(lib, dWs=None) == INVALID                 # K_s > 0 needs dW_shared
+    assert _bwd(lib, db=8) == ALIGNMENT
+    assert _bwd(lib, wsb=1024) == WORKSPACE
+    assert _bwd(lib, du=16) == INVALID                    # du overlaps u
+    assert "du overlaps u" in lib.moe_last_error().decode()
+    assert _bwd(lib, du=(1 << 20) + 64) == INVALID        # du overlaps dh
+    assert _bwd(lib, du=(1 << 44) + 256) == INVALID       # du overlaps the workspace
+    assert _bwd(lib, dWr=(1 << 44) - 4096) == INVALID     # dW_routed overlaps the workspace
+    assert _bwd(lib, K=65) == INVALID
+    assert _bwd(lib, T=0, u=None, dh=None, du=None, ws=None, wsb=0) == OK
+
+
+def test_backward_binding_refuses_host_tensors():
+    import torch
+    u = torch.zeros(4, 64)
+    with pytest.raises(mx.MoEError):
+        mx.layer_backward(u, torch.zeros(8, 64), torch.zeros(8 * 3 * 64 * 64), None, 8, 2, 0,
+                          torch.zeros(4, 64))
