@@ -5,6 +5,7 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-
 A step is one full layer forward (router, dispatch, grouped SwiGLU expert
 GEMMs with the shared experts in the same launches, combine) over one batch
 of seeded synthetic hidden states, with every input already resident in HBM.
+The layer backward (all gradients, routing recomputed) is timed beside it.
 The default workload is the 16B-model-shaped prefill layer in bfloat16
 (T=8192 tokens, d=2048, 64 routed + 2 shared experts, top-6, intermediate
 1408).  The decode-shaped batch (T=64, same layer) is timed beside it.
@@ -36,6 +37,10 @@ def parse():
     ap.add_argument("--decode-workload", default="moe16b_decode_bf16")
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the layer backward beside the forward")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the layer backward of the workload (for profiling runs)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--sweep", action="store_true",
                     help="granularity sweep instead of the benchmark line: the same layer "
@@ -114,6 +119,38 @@ def time_layer(mx, t, w, steps, warmup, stage_timing):
     return start.elapsed_time(stop), stages
 
 
+def time_backward(mx, t, w, steps, warmup):
+    """Warm up, then time exactly `steps` layer backwards (routing recomputed, every
+    gradient written) between two synchronisations; returns elapsed ms."""
+    import torch
+
+    g = torch.Generator(device=t["u"].device)
+    g.manual_seed(w.seed + 7)
+    dh = torch.randn(t["u"].shape, generator=g, device=t["u"].device, dtype=t["u"].dtype)
+    I = t["Wr"].numel() // (3 * w.N * w.d)
+    ws = torch.empty(mx.backward_workspace_size(w.T, w.d, I, w.N, w.K, w.K_s,
+                                                1 if w.dtype == "bf16" else 0),
+                     dtype=torch.uint8, device=t["u"].device)
+    args = (t["u"], t["E"], t["Wr"], t["Ws"], w.N, w.K, w.K_s, dh, t["bias"])
+    for _ in range(warmup):
+        out = mx.layer_backward(*args, workspace=ws)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        out = mx.layer_backward(*args, workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    del out, ws
+    return start.elapsed_time(stop)
+
+
+def backward_flops(w, I):
+    """MFMA FLOPs of one backward: per expert slot the recomputed gate/up product (4dI),
+    dP (2dI), dx (4dI), dW_down (2dI), dW_gate and dW_up (4dI); dE_gate 2Nd per token."""
+    return 16.0 * w.d * I * w.T * (w.K + w.K_s) + 2.0 * w.N * w.d * w.T
+
+
 def experts_hit(mx, t, w):
     """Distinct routed experts selected in the batch (the decode weights actually streamed)."""
     idx, _, _ = mx.route(t["u"], t["E"], w.K, t["bias"])
@@ -181,6 +218,22 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
+def backward_only(args):
+    import torch
+
+    import moe_inputs
+    import mixture_experts_ffn_fp32_amd as mx
+
+    dev = torch.device("cuda:0")
+    inp = moe_inputs.make(args.workload)
+    w = inp.w
+    t = upload(inp, dev)
+    ms = time_backward(mx, t, w, args.steps, args.warmup) / args.steps
+    fl = backward_flops(w, w.I)
+    print(json.dumps({"backward": w.name, "ms_per_step": round(ms, 4),
+                      "tflops": round(fl / (ms / 1e3) / 1e12, 2)}), flush=True)
+
+
 def traffic_record(kernel_src: str, key: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source (else None)."""
@@ -206,6 +259,8 @@ def main():
         return profile_mode(args)
     if args.sweep:
         return sweep(args)
+    if args.backward_only:
+        return backward_only(args)
     import torch
 
     import moe_inputs
@@ -236,6 +291,15 @@ def main():
                 "algorithmic_flops_per_launch": g1_flops}
     stage_ms = {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items()}
     layer_tflops = flops_step / (ms_step / 1e3) / 1e12
+    backward = None
+    if not args.no_backward:
+        bsteps = max(1, args.steps // 2)
+        bms = time_backward(mx, t, w, bsteps, 1) / bsteps
+        bflops = backward_flops(w, w.I)
+        backward = {"workload": w.name, "ms_per_step": round(bms, 4),
+                    "tokens_per_s": round(w.T / (bms / 1e3), 1), "steps": bsteps,
+                    "mfma_flops": bflops, "tflops": round(bflops / (bms / 1e3) / 1e12, 2),
+                    "mfma_frac": round(bflops / (bms / 1e3) / 1e12 / peak, 4)}
     del t
     torch.cuda.empty_cache()
 
@@ -276,6 +340,7 @@ def main():
         "stage_ms": stage_ms,
         "roofline": roofline,
         "decode": decode,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

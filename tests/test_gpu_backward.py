@@ -111,3 +111,13 @@ def test_backward_empty_batch():
     torch.cuda.synchronize()
     assert du.shape == (0, w.d)
     assert torch.count_nonzero(dWr).item() == 0 and torch.count_nonzero(dE).item() == 0
+
+
+@pytest.mark.timeout(600)
+def test_layer_backward_16b_prefill_full():
+    """The 16B-shaped prefill layer (T=8192, d=2048, 64 routed + 2 shared experts,
+    top-6, I=1408, bf16) in the launch configuration the benchmark times: every
+    gradient element against the float64 oracle (about 15 s of CPU)."""
+    up = Uploaded(moe_inputs.make("moe16b_prefill_bf16"))
+    out, idx, gate = run_backward(up)
+    check_gradients(up.w, out, reference(up, idx, gate))
