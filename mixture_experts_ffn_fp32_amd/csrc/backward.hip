@@ -445,39 +445,70 @@ __global__ __launch_bounds__(256) void bw_softmax_kernel(BwdArgs a, const float*
   }
 }
 
+// Eight consecutive elements of the storage type as float32, and back.
+__device__ __forceinline__ void bw_load8(const uint16_t* p, float (&o)[8]) {
+  const u32x4 v = *(const u32x4*)p;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[2 * e] = __uint_as_float(v[e] << 16);
+    o[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void bw_load8(const float* p, float (&o)[8]) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = a[e];
+    o[4 + e] = b[e];
+  }
+}
+__device__ __forceinline__ void bw_store8(uint16_t* p, const float (&v)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = (uint32_t)f32_to_bf16(v[2 * e]) | ((uint32_t)f32_to_bf16(v[2 * e + 1]) << 16);
+  *(u32x4*)p = w;
+}
+__device__ __forceinline__ void bw_store8(float* p, const float (&v)[8]) {
+  *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+  *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 // du_t = dh_t + sum_k dX[slot_of(t, k)] + sum_j dXs[j][t] + E_gate^T dz_t, one
-// float32 sum in that order, rounded once.  One thread per 4 output columns.
+// float32 sum in that order, rounded once.  One block per token, eight
+// columns per thread; the token's dz row is read once into LDS.
 template <class E>
 __global__ __launch_bounds__(256) void bw_du_kernel(BwdArgs a, const int32_t* __restrict__ slot_of,
                                                     const float* __restrict__ dz, void* du) {
   using Tp = typename E::T;
-  const int q = blockIdx.x * 256 + threadIdx.x, per = a.d / 4;
-  const int t = q / per, n = (q % per) * 4;
-  if (t >= a.T) return;
-  float acc[4];
-  const Tp* dhr = (const Tp*)a.dh + (size_t)t * a.d + n;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = load_as_f32<E>(dhr + e);
-  for (int k = 0; k < a.K; ++k) {
-    const int sl = slot_of[(size_t)t * a.K + k];
-    const f32x4 v = *(const f32x4*)(a.dX + (size_t)sl * a.d + n);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += v[e];
-  }
-  for (int j = 0; j < a.K_s; ++j) {
-    const f32x4 v = *(const f32x4*)(a.dXs + ((size_t)j * a.T + t) * a.d + n);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += v[e];
-  }
+  __shared__ float s_dz[256];
+  __shared__ int s_slot[256];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < a.N; i += 256) s_dz[i] = dz[(size_t)t * a.N + i];
+  for (int k = tid; k < a.K; k += 256) s_slot[k] = slot_of[(size_t)t * a.K + k];
+  __syncthreads();
   const Tp* Eg = (const Tp*)a.E_gate;
-  for (int i = 0; i < a.N; ++i) {
-    const float z = dz[(size_t)t * a.N + i];
+  for (int n = tid * 8; n < a.d; n += 256 * 8) {
+    float acc[8], v[8];
+    bw_load8((const Tp*)a.dh + (size_t)t * a.d + n, acc);
+    for (int k = 0; k < a.K; ++k) {
+      bw_load8(a.dX + (size_t)s_slot[k] * a.d + n, v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += z * load_as_f32<E>(Eg + (size_t)i * a.d + n + e);
+      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
+    for (int j = 0; j < a.K_s; ++j) {
+      bw_load8(a.dXs + ((size_t)j * a.T + t) * a.d + n, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
+    for (int i = 0; i < a.N; ++i) {
+      const float z = s_dz[i];
+      bw_load8(Eg + (size_t)i * a.d + n, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += z * v[e];
+    }
+    bw_store8((Tp*)du + (size_t)t * a.d + n, acc);
   }
-  Tp* o = (Tp*)du + (size_t)t * a.d + n;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) store_from_f32<E>(o + e, acc[e]);
 }
 
 // dE_gate = sum of the per-chunk partials, in chunk order.
@@ -490,25 +521,21 @@ __global__ __launch_bounds__(256) void bw_de_reduce_kernel(const float* __restri
   dE[q] = acc;
 }
 
-// db_i = sum_t dz[t][i]: per-chunk float64 partial sums, then one block in order.
-constexpr int kBwRows = 256;
-__global__ __launch_bounds__(256) void bw_db_partial_kernel(const float* __restrict__ dz, int T,
-                                                            int N, double* __restrict__ part) {
-  const int b = blockIdx.x;
-  for (int i = threadIdx.x; i < N; i += 256) {
-    double acc = 0.0;
-    const int t1 = min((b + 1) * kBwRows, T);
-    for (int t = b * kBwRows; t < t1; ++t) acc += dz[(size_t)t * N + i];
-    part[(size_t)b * N + i] = acc;
+// db_i = sum_t dz[t][i]: one block per expert, float64 partial sums per
+// thread over a fixed token stride, then a fixed-order tree.
+__global__ __launch_bounds__(256) void bw_db_kernel(const float* __restrict__ dz, int T, int N,
+                                                    float* __restrict__ db) {
+  __shared__ double red[256];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  double acc = 0.0;
+  for (int t = tid; t < T; t += 256) acc += dz[(size_t)t * N + i];
+  red[tid] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
   }
-}
-__global__ __launch_bounds__(256) void bw_db_final_kernel(const double* __restrict__ part, int nb,
-                                                          int N, float* __restrict__ db) {
-  for (int i = threadIdx.x; i < N; i += 256) {
-    double acc = 0.0;
-    for (int b = 0; b < nb; ++b) acc += part[(size_t)b * N + i];
-    db[i] = (float)acc;
-  }
+  if (tid == 0) db[i] = (float)red[0];
 }
 
 template <class E, int G>
@@ -541,7 +568,7 @@ hipError_t bg_launch(const BwdArgs& a, int32_t* tab, hipStream_t st) {
 template <class E>
 hipError_t backward_t(const BwdArgs& a, const float* gate, const float* scores,
                       const int32_t* idx, float* ds_pair, int32_t* slot_of, float* dz,
-                      double* db_part, float* dgate_bias, void* du, int32_t* tab,
+                      float* dgate_bias, void* du, int32_t* tab,
                       hipStream_t st) {
   hipError_t e;
   const int TK = a.T * a.K;
@@ -563,13 +590,46 @@ hipError_t backward_t(const BwdArgs& a, const float* gate, const float* scores,
                                                           a.dE_gate);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  bw_du_kernel<E><<<((size_t)a.T * (a.d / 4) + 255) / 256, 256, 0, st>>>(a, slot_of, dz, du);
+  bw_du_kernel<E><<<a.T, 256, 0, st>>>(a, slot_of, dz, du);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (dgate_bias != nullptr) {
-    const int nb = (a.T + kBwRows - 1) / kBwRows;
-    bw_db_partial_kernel<<<nb, 256, 0, st>>>(dz, a.T, a.N, db_part);
+    bw_db_kernel<<<a.N, 256, 0, st>>>(dz, a.T, a.N, dgate_bias);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    bw_db_final_kernel<<<1, 256, 0, st>>>(db_part, nb, a.N, dgate_bias);
+  }
+  return hipSuccess;
+}
+
+// bfloat16: every expert-slot product on the pipelined k-major GEMM
+// (backward_gemm.hip); the router gradient and the sums here.
+hipError_t backward_pipe_bf16(const BwdArgs& a, const float* scores, const int32_t* idx,
+                              float* ds_pair, int32_t* slot_of, float* dz,
+                              float* dgate_bias, void* du, int32_t* tab, int32_t* tabs,
+                              hipStream_t st) {
+  using E = ElemBF16;
+  hipError_t e;
+  const int TK = a.T * a.K;
+  if ((e = launch_bt_prep(a, tabs, st)) != hipSuccess) return e;
+  if ((e = launch_bt_gemm(1, a, tabs, st)) != hipSuccess) return e;  // dP
+  if ((e = launch_bt_gemm(2, a, tabs, st)) != hipSuccess) return e;  // a, c and the SwiGLU backward
+  bw_slot_of_kernel<<<(TK + 255) / 256, 256, 0, st>>>(a.sorted_pair, TK, slot_of);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_bt_ds(a, slot_of, ds_pair, st)) != hipSuccess) return e;
+  bw_softmax_kernel<E><<<(a.T + 3) / 4, 256, 0, st>>>(a, scores, idx, ds_pair, dz);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = bg_launch<E, BG_DE>(a, tab, st)) != hipSuccess) return e;
+  {
+    const int Nd = a.N * a.d;
+    bw_de_reduce_kernel<<<(Nd + 255) / 256, 256, 0, st>>>(a.dE_part, bg_groups<BG_DE>(a), Nd,
+                                                          a.dE_gate);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = launch_bt_gemm(3, a, tabs, st)) != hipSuccess) return e;  // dx
+  bw_du_kernel<E><<<a.T, 256, 0, st>>>(a, slot_of, dz, du);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_bt_gemm(4, a, tabs, st)) != hipSuccess) return e;  // dW_down
+  if ((e = launch_bt_gemm(5, a, tabs, st)) != hipSuccess) return e;  // dW_gate, dW_up
+  if (dgate_bias != nullptr) {
+    bw_db_kernel<<<a.N, 256, 0, st>>>(dz, a.T, a.N, dgate_bias);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -577,17 +637,19 @@ hipError_t backward_t(const BwdArgs& a, const float* gate, const float* scores,
 
 }  // namespace
 
-int backward_db_blocks(int T) { return (T + kBwRows - 1) / kBwRows; }
 int backward_de_chunks(int T) { return (T + kBgDeRows - 1) / kBgDeRows; }
 
 hipError_t launch_backward(int dtype, const BwdArgs& a, const float* gate, const float* scores,
                            const int32_t* idx, float* ds_pair, int32_t* slot_of, float* dz,
-                           double* db_part, float* dgate_bias, void* du, int32_t* tab,
-                           hipStream_t stream) {
+                           float* dgate_bias, void* du, int32_t* tab,
+                           int32_t* tabs, hipStream_t stream) {
+  if (dtype == 1 && tabs != nullptr)
+    return backward_pipe_bf16(a, scores, idx, ds_pair, slot_of, dz, dgate_bias, du, tab,
+                              tabs, stream);
   if (dtype == 1)
-    return backward_t<ElemBF16>(a, gate, scores, idx, ds_pair, slot_of, dz, db_part, dgate_bias,
+    return backward_t<ElemBF16>(a, gate, scores, idx, ds_pair, slot_of, dz, dgate_bias,
                                 du, tab, stream);
-  return backward_t<ElemF32>(a, gate, scores, idx, ds_pair, slot_of, dz, db_part, dgate_bias, du,
+  return backward_t<ElemF32>(a, gate, scores, idx, ds_pair, slot_of, dz, dgate_bias, du,
                              tab, stream);
 }
 

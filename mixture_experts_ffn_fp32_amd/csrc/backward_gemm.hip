@@ -1,0 +1,690 @@
+// Pipelined bfloat16 backward of the DeepSeekMoE layer (DeepSeekMoE paper
+// summary, papercache.org, sec. 3.2 layer equation, differentiated by the
+// chain rule with each token's top-K set held fixed).
+//
+// Every expert-slot product of the backward runs as a grouped GEMM whose two
+// operands are contiguous along the contraction ("k-major"), so all of them
+// share one LDS-DMA MFMA pipeline: tiles of 256 x 256, eight wavefronts of
+// 64 x 128, 128-byte k-steps landing by direct-to-LDS loads in a two-slot ring
+// while the other slot is multiplied.  Operands that are naturally laid out
+// along the output dimension are transposed once beforehand:
+//
+//   WdT  = W_down^T, WguT = [W_gate; W_up]^T             (per virtual expert)
+//   XT, dhT = u^T, dh^T over padded slot columns          (gathered by dispatch)
+//
+// Products, per virtual expert v (routed: its slots; shared: every token):
+//   DP   dP[slot][i]   = dh_tok . WdT[i]                  (K = d)
+//   AC   [a c][slot][i] = u_tok . [W_gate; W_up][i]        (K = d), fused epilogue:
+//        p = SiLU(a) c, da = g dP c SiLU'(a), dc = g dP SiLU(a),
+//        writes dAC (slot-major), dACT and (g p)^T (column-major), and the
+//        partial gate gradients sum_i dP p per 128 columns
+//   DX   dx[slot][n]   = dAC[slot] . WguT[n]              (K = 2I)
+//   DWD  dW_down[n][i] = dhT[n] . gPT[i]                  (K = the expert's padded slots)
+//   DWGC dW_gu[j][n]   = dACT[j] . XT[n]                  (K = the same)
+// Padded slot columns hold zeros, so a contraction over them needs no mask.
+#include "lds_dma.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+enum : int { BT_DP = 1, BT_AC = 2, BT_DX = 3, BT_DWD = 4, BT_DWGC = 5, BT_NG = 5 };
+constexpr int kBtBM = 256, kBtBNB = 256, kBtRB = 128;  // A rows, B rows, k bytes per step
+constexpr int kBtSlot = (kBtBM + kBtBNB) * kBtRB;      // 64 KB
+constexpr int kBtThreads = 512, kBtNI = 8;             // DMA instructions per wavefront per step
+constexpr int kBtMaxV = 256 + 16;
+
+__host__ __device__ constexpr int bt_bn(int G) { return G == BT_AC ? kBtBNB / 2 : kBtBNB; }
+
+__device__ __forceinline__ int bt_xcd_swizzle(int b, int G) {
+  const int x = b & 7, q = G >> 3, r = G & 7;
+  return x * q + min(x, r) + (b >> 3);
+}
+
+struct BtGroup {
+  int M, Nc, steps, rows, base;
+  bool routed;
+};
+
+// Geometry of virtual expert v in product G.
+template <int G>
+__device__ __forceinline__ BtGroup bt_group(const BwdArgs& a, int v) {
+  BtGroup g;
+  const int TK = a.T * a.K;
+  g.routed = v < a.N;
+  if (g.routed) {
+    g.base = min(max(a.offsets[v], 0), TK);
+    g.rows = min(max(a.offsets[v + 1], g.base), TK) - g.base;
+  } else {
+    g.base = 0;
+    g.rows = a.T;
+  }
+  const int kpad = (g.rows + 63) >> 6;
+  switch (G) {
+    case BT_DP: g.M = g.rows; g.Nc = a.I; g.steps = a.d >> 6; break;
+    case BT_AC: g.M = g.rows; g.Nc = a.I; g.steps = a.d >> 6; break;
+    case BT_DX: g.M = g.rows; g.Nc = a.d; g.steps = a.I >> 5; break;
+    case BT_DWD: g.M = a.d; g.Nc = a.I; g.steps = kpad; break;
+    default: g.M = 2 * a.I; g.Nc = a.d; g.steps = kpad; break;
+  }
+  return g;
+}
+
+template <int G>
+__device__ __forceinline__ int bt_tiles(const BwdArgs& a, int v) {
+  const BtGroup g = bt_group<G>(a, v);
+  return g.M > 0 ? ((g.M + kBtBM - 1) / kBtBM) * ((g.Nc + bt_bn(G) - 1) / bt_bn(G)) : 0;
+}
+
+// First padded column of virtual expert v in XT / dhT (shared experts share one range).
+__device__ __forceinline__ long long bt_colx(const BwdArgs& a, int v) {
+  return v < a.N ? a.pcol[v] : a.pcol[a.N];
+}
+// ... and in dACT / gPT (one range per shared expert).
+__device__ __forceinline__ long long bt_colp(const BwdArgs& a, int v) {
+  return v < a.N ? a.pcol[v] : a.pcol[a.N] + (long long)(v - a.N) * a.Tp;
+}
+
+// Group order of product G's tile table.  The weight-gradient products
+// contract over an expert's slots, so a shared expert's tiles (all T tokens)
+// are many times longer than a routed expert's: they go first, so the long
+// tiles start at once and the short ones fill in behind them.
+template <int G>
+__device__ __forceinline__ int bt_order(const BwdArgs& a, int k) {
+  if (G == BT_DWD || G == BT_DWGC) return k < a.K_s ? a.N + k : k - a.K_s;
+  return k;
+}
+
+template <int G>
+__device__ __forceinline__ void bt_table_one(const BwdArgs& a, int lane, int V,
+                                             int32_t* __restrict__ out) {
+  int carry = 0;
+  for (int b = 0; b < V; b += 64) {
+    const int k = b + lane;
+    const int t = k < V ? bt_tiles<G>(a, bt_order<G>(a, k)) : 0;
+    int inc = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (k < V) out[k] = carry + inc - t;
+    carry += __shfl(inc, 63);
+  }
+  if (lane == 0) out[V] = carry;
+}
+
+// Padded column offsets of the routed experts and the tile prefix of every
+// product (one wavefront).
+__global__ __launch_bounds__(64) void bt_table_kernel(BwdArgs a, int32_t* __restrict__ tabs) {
+  const int lane = threadIdx.x, V = a.N + a.K_s;
+  int carry = 0;
+  for (int b = 0; b < a.N; b += 64) {
+    const int v = b + lane;
+    int c = 0;
+    if (v < a.N) c = (bt_group<BT_DP>(a, v).rows + 63) & ~63;
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (v < a.N) a.pcol[v] = carry + inc - c;
+    carry += __shfl(inc, 63);
+  }
+  if (lane == 0) a.pcol[a.N] = carry;
+  bt_table_one<BT_DP>(a, lane, V, tabs + 0 * (V + 1));
+  bt_table_one<BT_AC>(a, lane, V, tabs + 1 * (V + 1));
+  bt_table_one<BT_DX>(a, lane, V, tabs + 2 * (V + 1));
+  bt_table_one<BT_DWD>(a, lane, V, tabs + 3 * (V + 1));
+  bt_table_one<BT_DWGC>(a, lane, V, tabs + 4 * (V + 1));
+}
+
+// ---------------------------------------------------------------- transposes
+// Out[c][r] = In_r[c] over 64 x 64 tiles (bfloat16), through LDS.
+//  MODE 0: W_down^T per virtual expert (In rows n < d of I columns; z = v)
+//  MODE 1: [W_gate; W_up]^T            (In rows j < 2I of d columns; z = v)
+//  MODE 2: u^T (z = 0) and dh^T (z = 1) over the padded slot columns; row r
+//          is the token of padded column r, zero in the padding.
+template <int MODE>
+__global__ __launch_bounds__(256) void bt_transpose_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, z = blockIdx.z;
+  const size_t Id = (size_t)a.I * a.d;
+  const uint16_t* src = nullptr;  // row r0 of the input (MODE 0, 1)
+  size_t src_ld = 0;
+  uint16_t* dst;
+  size_t dst_ld;
+  // MODE 2: the virtual range this 64-column block lies in
+  int rv_lo = 0, rv_rows = 0, rv_slot0 = 0;
+  bool rv_routed = false;
+  if (MODE < 2) {
+    const uint16_t* W = z < a.N ? (const uint16_t*)a.W_routed + (size_t)z * 3 * Id
+                                : (const uint16_t*)a.W_shared + (size_t)(z - a.N) * 3 * Id;
+    if (MODE == 0) {
+      src = W + 2 * Id;
+      src_ld = a.I;
+      dst = (uint16_t*)a.WdT + (size_t)z * Id;
+      dst_ld = a.d;
+    } else {
+      src = W;
+      src_ld = a.d;
+      dst = (uint16_t*)a.WguT + (size_t)z * 2 * Id;
+      dst_ld = 2 * (size_t)a.I;
+    }
+  } else {
+    const int R = a.pcol[a.N];
+    if (r0 >= R + a.Tp) return;
+    if (r0 >= R) {
+      rv_lo = R;
+      rv_rows = a.T;
+    } else {
+      int lo = 0, hi = a.N - 1;  // last routed expert whose range starts at or before r0
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.pcol[mid] <= r0) lo = mid; else hi = mid - 1;
+      }
+      const int TK = a.T * a.K;
+      rv_routed = true;
+      rv_lo = a.pcol[lo];
+      rv_slot0 = min(max(a.offsets[lo], 0), TK);
+      rv_rows = min(max(a.offsets[lo + 1], rv_slot0), TK) - rv_slot0;
+    }
+    dst = (uint16_t*)(z == 0 ? a.XT : a.dhT);
+    dst_ld = (size_t)a.ldx;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = tid + h * 256, r = q >> 3, ch = q & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (MODE < 2) {
+      v = *(const u32x4*)(src + (size_t)(r0 + r) * src_ld + c0 + ch * 8);
+    } else {
+      const int local = r0 + r - rv_lo;
+      if (local < rv_rows) {
+        int tok = local;
+        if (rv_routed) {
+          const int TK = a.T * a.K;
+          const int p = a.sorted_pair[rv_slot0 + local];
+          tok = ((unsigned)p < (unsigned)TK) ? p / a.K : 0;
+        }
+        const uint16_t* row = (const uint16_t*)(z == 0 ? a.u : a.dh) + (size_t)tok * a.d;
+        v = *(const u32x4*)(row + c0 + ch * 8);
+      }
+    }
+    *(u32x4*)&tile[r][ch * 8] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = tid + h * 256, c = q >> 3, rc = q & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)tile[rc * 8 + 2 * k][c] | ((uint32_t)tile[rc * 8 + 2 * k + 1][c] << 16);
+    *(u32x4*)(dst + (size_t)(c0 + c) * dst_ld + r0 + rc * 8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// ---------------------------------------------------------------- operand rows
+// Start (k = 0) of row m of A and row r of B's tile for group v; rows are
+// clamped to the group's extent (the repeats are never stored).
+template <int G>
+__device__ __forceinline__ const uint8_t* bt_a_row(const BwdArgs& a, int v, const BtGroup& g,
+                                                   int m) {
+  const int j = v - a.N;
+  switch (G) {
+    case BT_DP:
+    case BT_AC: {
+      int tok = m;
+      if (g.routed) {
+        const int TK = a.T * a.K;
+        const int p = a.sorted_pair[g.base + m];
+        tok = ((unsigned)p < (unsigned)TK) ? p / a.K : 0;
+      }
+      return (const uint8_t*)((const uint16_t*)(G == BT_DP ? a.dh : a.u) + (size_t)tok * a.d);
+    }
+    case BT_DX:
+      return (const uint8_t*)(g.routed
+                                  ? (const uint16_t*)a.dAC + (size_t)(g.base + m) * 2 * a.I
+                                  : (const uint16_t*)a.dACs + ((size_t)m * a.K_s + j) * 2 * a.I);
+    case BT_DWD:
+      return (const uint8_t*)((const uint16_t*)a.dhT + (size_t)m * a.ldx + bt_colx(a, v));
+    default:
+      return (const uint8_t*)((const uint16_t*)a.dACT + (size_t)m * a.ldp + bt_colp(a, v));
+  }
+}
+
+template <int G>
+__device__ __forceinline__ const uint8_t* bt_b_row(const BwdArgs& a, int v, int n0, int r) {
+  const size_t Id = (size_t)a.I * a.d;
+  switch (G) {
+    case BT_DP:
+      return (const uint8_t*)((const uint16_t*)a.WdT + (size_t)v * Id +
+                              (size_t)min(n0 + r, a.I - 1) * a.d);
+    case BT_AC: {
+      const uint16_t* W = v < a.N ? (const uint16_t*)a.W_routed + (size_t)v * 3 * Id
+                                  : (const uint16_t*)a.W_shared + (size_t)(v - a.N) * 3 * Id;
+      // the first half of the B tile: W_gate rows of the tile's columns; the
+      // second half: W_up rows of the same columns
+      const int half = kBtBNB / 2;
+      const int i = r < half ? min(n0 + r, a.I - 1) : a.I + min(n0 + r - half, a.I - 1);
+      return (const uint8_t*)(W + (size_t)i * a.d);
+    }
+    case BT_DX:
+      return (const uint8_t*)((const uint16_t*)a.WguT + (size_t)v * 2 * Id +
+                              (size_t)min(n0 + r, a.d - 1) * 2 * a.I);
+    case BT_DWD:
+      return (const uint8_t*)((const uint16_t*)a.gPT + (size_t)min(n0 + r, a.I - 1) * a.ldp +
+                              bt_colp(a, v));
+    default:
+      return (const uint8_t*)((const uint16_t*)a.XT + (size_t)min(n0 + r, a.d - 1) * a.ldx +
+                              bt_colx(a, v));
+  }
+}
+
+// B tile row of wavefront column wn's fragment fn: AC pairs gate fragment fn
+// with the up fragment fn + 2 of the same columns.
+template <int G>
+__device__ __forceinline__ int bt_bcol(int wn, int fn) {
+  if (G == BT_AC) return fn < 2 ? (wn * 2 + fn) * 32 : kBtBNB / 2 + (wn * 2 + fn - 2) * 32;
+  return (wn * 4 + fn) * 32;
+}
+
+__device__ __forceinline__ f32x16 bt_mfma(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int G>
+__device__ __forceinline__ void bt_frags(const uint8_t* __restrict__ rd, int kg, int wm, int wn,
+                                         int lane, u32x4 (&af)[2], u32x4 (&bfr)[4]) {
+  const int ch = kg * 2 + (lane >> 5);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+    af[fm] = *(const u32x4*)(rd + lds_chunk_offset(wm * 64 + fm * 32 + (lane & 31), ch));
+#pragma unroll
+  for (int fn = 0; fn < 4; ++fn)
+    bfr[fn] = *(const u32x4*)(rd + lds_chunk_offset(kBtBM + bt_bcol<G>(wn, fn) + (lane & 31), ch));
+}
+
+// One k-step out of ring slot `rd`.  The next k-step's direct-to-LDS loads
+// (base `db`, lane offsets `off`, into `wr`; `nrec` = 0 after the last k-step
+// makes them return zeros without touching memory) are interleaved with the
+// MFMAs of the first two k-groups, and the next k-group's fragments are read
+// after each MFMA.  (One instance in the loop: a second, load-free copy for
+// the last k-step doubles the live ranges and spills.)
+template <int G, bool ISSUE = true>
+__device__ __forceinline__ void bt_mma(const uint8_t* __restrict__ rd, int wm, int wn, int lane,
+                                       f32x16 (&acc)[2][4], const uint8_t* db,
+                                       const uint32_t (&off)[kBtNI], uint8_t* __restrict__ wr,
+                                       int nrec) {
+  constexpr int KG = kBtRB / 32, PARTS = 2, PER = kBtNI / PARTS;
+  u32x4 af[2][2], bfr[2][4];
+  bt_frags<G>(rd, 0, wm, wn, lane, af[0], bfr[0]);
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg) {
+    if (ISSUE && kg < PARTS) {
+#pragma unroll
+      for (int i = kg * PER; i < (kg + 1) * PER; ++i) dma16(db, off[i], wr + i * 1024, nrec);
+    }
+    if (kg + 1 < KG) bt_frags<G>(rd, kg + 1, wm, wn, lane, af[(kg + 1) & 1], bfr[(kg + 1) & 1]);
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = bt_mfma(af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg) {
+    const int nr = kg + 1 < KG ? 6 : 0, nd = (ISSUE && kg < PARTS) ? PER : 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (m < nd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ float bt_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
+// Column-major store of a staged [128 columns][256 rows] bfloat16 tile: LDS
+// row i (16-byte chunk c at c ^ (i & 31)) goes to out row (row0 + i), columns
+// col0 + 8c .., for rows i < nrows and chunks c < nchunks.
+__device__ __forceinline__ void bt_store_t(const uint8_t* __restrict__ st, uint16_t* out,
+                                           long long ld, long long row0, long long col0,
+                                           int nrows, int nchunks) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int q = threadIdx.x + k * kBtThreads, i = q >> 5, c = q & 31;
+    if (i < nrows && c < nchunks) {
+      const u32x4 v = *(const u32x4*)(st + i * 512 + ((c ^ (i & 31)) << 4));
+      *(u32x4*)(out + (row0 + i) * ld + col0 + c * 8) = v;
+    }
+  }
+}
+
+// Grouped k-major GEMM C = A B^T for product G (bfloat16 operands, float32
+// accumulation).  One 256 x bt_bn(G) tile per block.
+template <int G>
+__global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
+                                                                const int32_t* __restrict__ tab) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBtSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBtSlot];
+  __shared__ int s_tab[kBtMaxV + 1];
+  __shared__ float s_gate[kBtBM];
+  __shared__ float s_ds[2][kBtBM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6), wm = wave >> 1, wn = wave & 1;
+  const int V = a.N + a.K_s;
+  for (int i = tid; i <= V; i += kBtThreads) s_tab[i] = tab[i];
+  __syncthreads();
+  const int total = s_tab[V];
+  if ((int)blockIdx.x >= total) return;
+  // slot-row products: consecutive tiles (m fastest: one weight tile, several
+  // token tiles) go to one XCD.  Weight-gradient products keep the launch
+  // order (longest tiles first); their m-tiles then fall on the XCDs in turn,
+  // and each XCD sees the same m-tile of every n-tile.
+  const int L = (G == BT_DWD || G == BT_DWGC) ? (int)blockIdx.x
+                                              : bt_xcd_swizzle(blockIdx.x, total);
+  int lo = 0, hi = V - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_tab[mid] <= L) lo = mid; else hi = mid - 1;
+  }
+  const int k_tab = lo;
+  const int v = uni(bt_order<G>(a, lo));
+  const BtGroup g = bt_group<G>(a, v);
+  constexpr int BN = bt_bn(G);
+  const int nmt = (g.M + kBtBM - 1) / kBtBM;
+  const int local = L - s_tab[k_tab];
+  const int m0 = uni((local % nmt) * kBtBM), n0 = uni((local / nmt) * BN);
+  const int steps = uni(g.steps);
+
+  if (G == BT_AC && tid < kBtBM) {
+    const int m = m0 + tid;
+    float gv = 0.f;  // rows past the expert's last slot contribute nothing
+    if (m < g.M) {
+      if (g.routed) {
+        const int TK = a.T * a.K;
+        const int p = a.sorted_pair[g.base + m];
+        gv = ((unsigned)p < (unsigned)TK) ? a.gate[p] : 0.f;
+      } else {
+        gv = 1.f;
+      }
+    }
+    s_gate[tid] = gv;
+  }
+
+  // this lane's direct-to-LDS rows: wavefronts 0-3 the A rows, 4-7 the B rows
+  const bool is_a = wave < 4;
+  const uint8_t* base;
+  uint32_t off[kBtNI];
+  {
+    const bool gathered = G == BT_DP || G == BT_AC;
+    const uint8_t* b0 = is_a ? (gathered ? (const uint8_t*)(G == BT_DP ? a.dh : a.u)
+                                         : bt_a_row<G>(a, v, g, min(m0, g.M - 1)))
+                             : bt_b_row<G>(a, v, n0, 0);
+    base = uni(b0);
+#pragma unroll
+    for (int i = 0; i < kBtNI; ++i) {
+      const int r = ((wave & 3) * kBtNI + i) * 8 + (lane >> 3);
+      const uint8_t* rp = is_a ? bt_a_row<G>(a, v, g, min(m0 + r, g.M - 1)) : bt_b_row<G>(a, v, n0, r);
+      const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+      off[i] = (uint32_t)(rp - base) + chunk * 16;
+    }
+  }
+  uint8_t* const w0 = lds0 + wave * kBtNI * 1024;
+  uint8_t* const w1 = lds1 + wave * kBtNI * 1024;
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (steps > 0) {
+#pragma unroll
+    for (int i = 0; i < kBtNI; ++i) dma16(base, off[i], w0 + i * 1024);
+  }
+  for (int s = 0; s < steps; ++s) {
+    pipe_sync();  // k-step s has landed; every wavefront is done with the other slot
+    const uint8_t* rd = (s & 1) ? lds1 : lds0;
+    uint8_t* wr = (s & 1) ? w0 : w1;
+    const bool more = s + 1 < steps;
+    bt_mma<G>(rd, wm, wn, lane, acc, uni(base + (size_t)(more ? s + 1 : 0) * kBtRB), off, wr,
+              more ? 0x7fffffff : 0);
+  }
+  pipe_sync();  // the ring is free for the epilogue (the zero loads have landed)
+
+  // acc[fm][fn][r]: tile row wm*64 + fm*32 + 8(r/4) + 4(lane/32) + r%4,
+  // tile column bt_bcol(wn, fn) + lane%32
+  const int lc = lane & 31, lh = lane >> 5;
+  if (G != BT_AC) {
+    const size_t Id = (size_t)a.I * a.d;
+    const int j = v - a.N;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (m >= g.M) continue;
+        float* c;
+        switch (G) {
+          case BT_DP:
+            c = g.routed ? a.dP + (size_t)(g.base + m) * a.I
+                         : a.dPs + ((size_t)m * a.K_s + j) * a.I;
+            break;
+          case BT_DX:
+            c = g.routed ? a.dX + (size_t)(g.base + m) * a.d : a.dXs + ((size_t)j * a.T + m) * a.d;
+            break;
+          case BT_DWD:
+            c = (g.routed ? a.dW_routed + (size_t)v * 3 * Id : a.dW_shared + (size_t)j * 3 * Id) +
+                2 * Id + (size_t)m * a.I;
+            break;
+          default:
+            c = (g.routed ? a.dW_routed + (size_t)v * 3 * Id : a.dW_shared + (size_t)j * 3 * Id) +
+                (size_t)m * a.d;
+            break;
+        }
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+          const int n = n0 + bt_bcol<G>(wn, fn) + lc;
+          if (n < g.Nc) c[n] = acc[fm][fn][r];
+        }
+      }
+    return;
+  }
+
+  // ---- AC epilogue: the SwiGLU backward of the tile
+  // dP of the tile's rows and columns, p, da, dc; dAC goes out slot-major from
+  // registers; da and dc are staged column-major ([column][row] bfloat16, 512
+  // bytes per column, chunk c at c ^ (column & 31)) in the two ring slots.
+  const int j = v - a.N;
+  // the tile's dP rows (routed: slot order; shared: token t, expert j)
+  const float* dp_base = g.routed ? a.dP + (size_t)g.base * a.I : a.dPs + (size_t)j * a.I;
+  const size_t dp_pitch = g.routed ? (size_t)a.I : (size_t)a.K_s * a.I;
+  uint16_t* dac_base = g.routed ? (uint16_t*)a.dAC + (size_t)g.base * 2 * a.I
+                                : (uint16_t*)a.dACs + (size_t)j * 2 * a.I;
+  const size_t dac_pitch = g.routed ? 2 * (size_t)a.I : (size_t)a.K_s * 2 * a.I;
+  float dsr[2][16];
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm) {
+    // all 32 dP values of this row fragment in flight at once
+    float dpv[2][16];
+#pragma unroll
+    for (int fp = 0; fp < 2; ++fp) {
+      const int i = n0 + bt_bcol<BT_AC>(wn, fp) + lc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        dpv[fp][r] = (m < g.M && i < a.I) ? dp_base[(size_t)m * dp_pitch + i] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dsr[fm][r] = 0.f;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int row0 = wm * 64 + fm * 32 + 8 * r4 + 4 * lh;  // tile rows row0 .. row0 + 3
+#pragma unroll
+      for (int fp = 0; fp < 2; ++fp) {
+        const int col = bt_bcol<BT_AC>(wn, fp) + lc;  // 0 .. 127
+        const int i = n0 + col;
+        float da[4], dc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = row0 + q;
+          const float dp = dpv[fp][4 * r4 + q];
+          const float av = acc[fm][fp][4 * r4 + q], cv = acc[fm][fp + 2][4 * r4 + q];
+          const float sg = bt_sigmoid(av), sl = av * sg;
+          const float p = sl * cv;
+          const float dpg = s_gate[t] * dp;
+          da[q] = dpg * cv * sg * (1.f + av * (1.f - sg));
+          dc[q] = dpg * sl;
+          dsr[fm][4 * r4 + q] += dp * p;
+        }
+        if (i < a.I) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m = m0 + row0 + q;
+            if (m < g.M) {
+              uint16_t* dacr = dac_base + (size_t)m * dac_pitch;
+              dacr[i] = f32_to_bf16(da[q]);
+              dacr[a.I + i] = f32_to_bf16(dc[q]);
+            }
+          }
+        }
+        const int sw = ((row0 >> 3) ^ (col & 31)) << 4;
+        uint2 wa, wc;
+        wa.x = pack_bf16x2(da[0], da[1]);
+        wa.y = pack_bf16x2(da[2], da[3]);
+        wc.x = pack_bf16x2(dc[0], dc[1]);
+        wc.y = pack_bf16x2(dc[2], dc[3]);
+        *(uint2*)(lds0 + col * 512 + sw + (row0 & 7) * 2) = wa;
+        *(uint2*)(lds1 + col * 512 + sw + (row0 & 7) * 2) = wc;
+      }
+    }
+  }
+  // partial gate gradients: sum over this wavefront's 64 columns, then the two
+  // column halves of the tile
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = dsr[fm][r];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
+      if (lc == 0) s_ds[wn][wm * 64 + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = x;
+    }
+  lds_sync();
+  const long long cp = bt_colp(a, v) + m0;
+  const int ncols = min(kBtBNB / 2, a.I - n0);
+  const int nch = (min(kBtBM, bt_pad64(g.M) - m0)) >> 3;  // 8-row chunks incl. zero padding
+  bt_store_t(lds0, (uint16_t*)a.dACT, a.ldp, n0, cp, ncols, nch);
+  bt_store_t(lds1, (uint16_t*)a.dACT, a.ldp, (long long)a.I + n0, cp, ncols, nch);
+  if (g.routed && tid < kBtBM && m0 + tid < g.M) {
+    const int NT = (a.I + kBtBNB / 2 - 1) / (kBtBNB / 2);
+    a.dsp[(size_t)(g.base + m0 + tid) * NT + n0 / (kBtBNB / 2)] = s_ds[0][tid] + s_ds[1][tid];
+  }
+  lds_sync();
+  // (g p)^T, recomputed from the accumulators
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int row0 = wm * 64 + fm * 32 + 8 * r4 + 4 * lh;
+#pragma unroll
+      for (int fp = 0; fp < 2; ++fp) {
+        const int col = bt_bcol<BT_AC>(wn, fp) + lc;
+        float gp[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float av = acc[fm][fp][4 * r4 + q], cv = acc[fm][fp + 2][4 * r4 + q];
+          gp[q] = s_gate[row0 + q] * (av * bt_sigmoid(av) * cv);
+        }
+        uint2 w;
+        w.x = pack_bf16x2(gp[0], gp[1]);
+        w.y = pack_bf16x2(gp[2], gp[3]);
+        *(uint2*)(lds0 + col * 512 + (((row0 >> 3) ^ (col & 31)) << 4) + (row0 & 7) * 2) = w;
+      }
+    }
+  lds_sync();
+  bt_store_t(lds0, (uint16_t*)a.gPT, a.ldp, n0, cp, ncols, nch);
+}
+
+// ds_pair[p] = sum of the partial gate gradients of p's slot, in column order.
+__global__ __launch_bounds__(256) void bt_ds_kernel(const float* __restrict__ dsp, int NT,
+                                                    const int32_t* __restrict__ slot_of, int TK,
+                                                    float* __restrict__ ds_pair) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= TK) return;
+  const float* s = dsp + (size_t)slot_of[p] * NT;
+  float x = 0.f;
+  for (int t = 0; t < NT; ++t) x += s[t];
+  ds_pair[p] = x;
+}
+
+long long bt_grid(int G, const BwdArgs& a) {
+  auto ct = [](long long x, long long b) { return (x + b - 1) / b; };
+  const long long TK = (long long)a.T * a.K, V = a.N + a.K_s;
+  const long long mt = (TK + (long long)a.N * (kBtBM - 1)) / kBtBM + a.K_s * ct(a.T, kBtBM);
+  switch (G) {
+    case BT_DP: return mt * ct(a.I, kBtBNB);
+    case BT_AC: return mt * ct(a.I, kBtBNB / 2);
+    case BT_DX: return mt * ct(a.d, kBtBNB);
+    case BT_DWD: return V * ct(a.d, kBtBM) * ct(a.I, kBtBNB);
+    default: return V * ct(2LL * a.I, kBtBM) * ct(a.d, kBtBNB);
+  }
+}
+
+template <int G>
+hipError_t bt_launch(const BwdArgs& a, const int32_t* tabs, hipStream_t st) {
+  const long long grid = bt_grid(G, a);
+  if (grid <= 0) return hipSuccess;
+  const int V = a.N + a.K_s;
+  bt_gemm_kernel<G><<<dim3((unsigned)grid), dim3(kBtThreads), 0, st>>>(a, tabs + (G - 1) * (V + 1));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bt_tables_ints(int N, int K_s) { return BT_NG * (N + K_s + 1); }
+
+hipError_t launch_bt_prep(const BwdArgs& a, int32_t* tabs, hipStream_t st) {
+  const int V = a.N + a.K_s;
+  bt_table_kernel<<<1, 64, 0, st>>>(a, tabs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bt_transpose_kernel<0><<<dim3(a.I / 64, a.d / 64, V), 256, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bt_transpose_kernel<1><<<dim3(a.d / 64, 2 * a.I / 64, V), 256, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bt_transpose_kernel<2><<<dim3(a.d / 64, (unsigned)(a.ldx / 64), 2), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bt_gemm(int G, const BwdArgs& a, const int32_t* tabs, hipStream_t st) {
+  switch (G) {
+    case BT_DP: return bt_launch<BT_DP>(a, tabs, st);
+    case BT_AC: return bt_launch<BT_AC>(a, tabs, st);
+    case BT_DX: return bt_launch<BT_DX>(a, tabs, st);
+    case BT_DWD: return bt_launch<BT_DWD>(a, tabs, st);
+    case BT_DWGC: return bt_launch<BT_DWGC>(a, tabs, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bt_ds(const BwdArgs& a, const int32_t* slot_of, float* ds_pair, hipStream_t st) {
+  const int TK = a.T * a.K, NT = (a.I + kBtBNB / 2 - 1) / (kBtBNB / 2);
+  bt_ds_kernel<<<(TK + 255) / 256, 256, 0, st>>>(a.dsp, NT, slot_of, TK, ds_pair);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,6 +1,8 @@
 // C ABI of the DeepSeekMoE layer forward: argument validation, workspace
 // layout and the stream-ordered launch sequence.  No device memory is
 // allocated here and nothing waits on the device (except moe_timing_read).
+#include <stdlib.h>
+
 #include <algorithm>
 #include <mutex>
 #include <string>
@@ -420,10 +422,22 @@ namespace {
 struct BwdLayout {
   size_t idx, gate, scores, rank, tile_counts, tile_base, counts, offsets, sorted_pair;
   size_t AC, ACs, dP, dPs, dAC, dACs, P, Ps, dY, dX, dXs, dzE, dz, dE_part, ds_pair, slot_of,
-      db_part, tab, total;
+      tab, total;
+  // pipelined bfloat16 path
+  bool pipe;
+  size_t WdT, WguT, XT, dhT, dACT, gPT, dsp, tabs;
+  long long ldx, ldp;
 };
 
 int pad8(int n) { return (n + 7) & ~7; }
+
+// bfloat16 backward on the pipelined GEMMs unless MOE_BWD_GENERIC=1 asks for
+// the generic kernels (the float32 path).
+bool bwd_pipe(int dtype) {
+  if (dtype != MOE_DTYPE_BF16) return false;
+  const char* s = getenv("MOE_BWD_GENERIC");
+  return !(s != nullptr && s[0] == '1');
+}
 
 BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype) {
   BwdLayout L{};
@@ -434,6 +448,8 @@ BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype)
     return at;
   };
   const size_t TK = (size_t)T * K, es = elem_size(dtype), nt = (size_t)rank_tiles(T);
+  L.pipe = bwd_pipe(dtype);
+  const size_t gen = L.pipe ? 0 : 1;  // buffers only the generic path uses
   L.idx = take(TK * 4);
   L.gate = take(TK * 4);
   L.scores = take((size_t)T * N * 4);
@@ -443,15 +459,15 @@ BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype)
   L.counts = take((size_t)N * 4);
   L.offsets = take((size_t)(N + 1) * 4);
   L.sorted_pair = take(TK * 4);
-  L.AC = take(TK * 2 * I * 4);
-  L.ACs = take((size_t)T * K_s * 2 * I * 4);
+  L.AC = take(gen * TK * 2 * I * 4);
+  L.ACs = take(gen * (size_t)T * K_s * 2 * I * 4);
   L.dP = take(TK * I * 4);
   L.dPs = take((size_t)T * K_s * I * 4);
   L.dAC = take(TK * 2 * I * es);
   L.dACs = take((size_t)T * K_s * 2 * I * es);
-  L.P = take(TK * I * es);
-  L.Ps = take((size_t)T * K_s * I * es);
-  L.dY = take(TK * d * es);
+  L.P = take(gen * TK * I * es);
+  L.Ps = take(gen * (size_t)T * K_s * I * es);
+  L.dY = take(gen * TK * d * es);
   L.dX = take(TK * d * 4);
   L.dXs = take((size_t)K_s * T * d * 4);
   L.dzE = take((size_t)T * pad8(N) * es);
@@ -459,8 +475,21 @@ BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype)
   L.dE_part = take((size_t)moe::backward_de_chunks(T) * N * d * 4);
   L.ds_pair = take(TK * 4);
   L.slot_of = take(TK * 4);
-  L.db_part = take((size_t)moe::backward_db_blocks(T) * N * 8);
   L.tab = take((size_t)(std::max(N + K_s, moe::backward_de_chunks(T)) + 1) * 4);
+  if (L.pipe) {
+    const size_t V = (size_t)N + K_s, Id = (size_t)I * d;
+    const long long R = moe::bt_routed_cols(T, K, N), Tp = moe::bt_pad64(T);
+    L.ldx = R + Tp;
+    L.ldp = R + (long long)K_s * Tp;
+    L.WdT = take(V * Id * 2);
+    L.WguT = take(V * 2 * Id * 2);
+    L.XT = take((size_t)d * L.ldx * 2);
+    L.dhT = take((size_t)d * L.ldx * 2);
+    L.dACT = take((size_t)2 * I * L.ldp * 2);
+    L.gPT = take((size_t)I * L.ldp * 2);
+    L.dsp = take(TK * ((I + 127) / 128) * 4);
+    L.tabs = take((size_t)(moe::bt_tables_ints(N, K_s) + N + 1) * 4);
+  }
   L.total = o;
   return L;
 }
@@ -555,10 +584,26 @@ moe_status_t moe_layer_backward(const void* u, const void* E_gate, const void* W
   a.K = K;
   a.K_s = K_s;
   a.NP = pad8(N);
+  a.gate = gate;
+  int32_t* tabs = nullptr;
+  if (L.pipe) {
+    tabs = (int32_t*)(ws + L.tabs);
+    a.WdT = ws + L.WdT;
+    a.WguT = ws + L.WguT;
+    a.XT = ws + L.XT;
+    a.dhT = ws + L.dhT;
+    a.dACT = ws + L.dACT;
+    a.gPT = ws + L.gPT;
+    a.dsp = (float*)(ws + L.dsp);
+    a.pcol = tabs + moe::bt_tables_ints(N, K_s);
+    a.ldx = L.ldx;
+    a.ldp = L.ldp;
+    a.Tp = moe::bt_pad64(T);
+  }
   if ((e = moe::launch_backward(dtype, a, gate, scores, idx, (float*)(ws + L.ds_pair),
                                 (int32_t*)(ws + L.slot_of), (float*)(ws + L.dz),
-                                (double*)(ws + L.db_part), dgate_bias, du,
-                                (int32_t*)(ws + L.tab), st)) != hipSuccess)
+                                dgate_bias, du,
+                                (int32_t*)(ws + L.tab), tabs, st)) != hipSuccess)
     return hip_fail(e, "backward launch");
   return ok();
 }

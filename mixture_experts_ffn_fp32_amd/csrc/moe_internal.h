@@ -145,13 +145,35 @@ struct BwdArgs {
   float* dW_routed;            // N weight blocks (float32)
   float* dW_shared;            // K_s weight blocks (float32)
   int T, d, I, N, K, K_s, NP;
+  // bfloat16 path (every product a k-major grouped GEMM on the LDS-DMA pipeline)
+  const float* gate;           // [T*K] kept gates by pair
+  void* WdT;                   // [V][I][d]   W_down^T per virtual expert (V = N + K_s)
+  void* WguT;                  // [V][d][2I]  [W_gate; W_up]^T
+  void* XT;                    // [d][ldx]    u^T over the padded slot columns
+  void* dhT;                   // [d][ldx]    dh^T over the same columns
+  void* dACT;                  // [2I][ldp]   [da, dc]^T over the padded slot columns
+  void* gPT;                   // [I][ldp]    (g p)^T
+  float* dsp;                  // [T*K][ceil(I/128)] partial gate gradients per 128 columns
+  int32_t* pcol;               // [N+1] padded first column of each routed expert
+  long long ldx, ldp;          // row pitches (elements) of XT/dhT and dACT/gPT
+  int Tp;                      // T rounded up to 64: the shared experts' column count
 };
-int backward_db_blocks(int T);
 int backward_de_chunks(int T);
+// Padded slot columns: every virtual expert's slots rounded up to 64.
+inline long long bt_routed_cols(int T, int K, int N) {
+  return (((long long)T * K + 63LL * N) + 63) / 64 * 64;
+}
+__host__ __device__ inline int bt_pad64(int x) { return (x + 63) & ~63; }
+int bt_tables_ints(int N, int K_s);
+hipError_t launch_bt_prep(const BwdArgs& a, int32_t* tabs, hipStream_t st);
+hipError_t launch_bt_gemm(int G, const BwdArgs& a, const int32_t* tabs, hipStream_t st);
+hipError_t launch_bt_ds(const BwdArgs& a, const int32_t* slot_of, float* ds_pair, hipStream_t st);
+// tabs: the pipelined bfloat16 path's tables (bt_tables_ints + N + 1 ints for
+// the padded columns), or NULL for the generic path.
 hipError_t launch_backward(int dtype, const BwdArgs& a, const float* gate, const float* scores,
                            const int32_t* idx, float* ds_pair, int32_t* slot_of, float* dz,
-                           double* db_part, float* dgate_bias, void* du, int32_t* tab,
-                           hipStream_t stream);
+                           float* dgate_bias, void* du, int32_t* tab,
+                           int32_t* tabs, hipStream_t stream);
 
 hipError_t launch_combine(int dtype, const void* u, const void* Y, const void* Y_shared, int T,
                           int d, int K, int K_s, void* h, hipStream_t stream);

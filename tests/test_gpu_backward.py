@@ -121,3 +121,13 @@ def test_layer_backward_16b_prefill_full():
     up = Uploaded(moe_inputs.make("moe16b_prefill_bf16"))
     out, idx, gate = run_backward(up)
     check_gradients(up.w, out, reference(up, idx, gate))
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "n63_bf16", "gran_m8_ks1_bf16"])
+def test_layer_backward_generic_kernels_bf16(name, monkeypatch):
+    """bfloat16 through the generic grouped kernels (the float32 path's) instead of
+    the pipelined ones: the same bar against the oracle."""
+    monkeypatch.setenv("MOE_BWD_GENERIC", "1")
+    up = Uploaded(small_inputs(name))
+    out, idx, gate = run_backward(up)
+    check_gradients(up.w, out, reference(up, idx, gate))
