@@ -22,6 +22,8 @@
 //   DWD  dW_down[n][i] = dhT[n] . gPT[i]                  (K = the expert's padded slots)
 //   DWGC dW_gu[j][n]   = dACT[j] . XT[n]                  (K = the same)
 // Padded slot columns hold zeros, so a contraction over them needs no mask.
+#include <algorithm>
+
 #include "lds_dma.h"
 #include "moe_internal.h"
 
@@ -138,6 +140,7 @@ __global__ __launch_bounds__(64) void bt_table_kernel(BwdArgs a, int32_t* __rest
   bt_table_one<BT_DX>(a, lane, V, tabs + 2 * (V + 1));
   bt_table_one<BT_DWD>(a, lane, V, tabs + 3 * (V + 1));
   bt_table_one<BT_DWGC>(a, lane, V, tabs + 4 * (V + 1));
+  if (lane < BT_NG * 8) tabs[BT_NG * (V + 1) + lane] = 0;  // claim counters
 }
 
 // ---------------------------------------------------------------- transposes
@@ -368,51 +371,66 @@ __device__ __forceinline__ void bt_store_t(const uint8_t* __restrict__ st, uint1
   }
 }
 
-// Grouped k-major GEMM C = A B^T for product G (bfloat16 operands, float32
-// accumulation).  One 256 x bt_bn(G) tile per block.
-template <int G>
-__global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
-                                                                const int32_t* __restrict__ tab) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBtSlot];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBtSlot];
-  __shared__ int s_tab[kBtMaxV + 1];
-  __shared__ float s_gate[kBtBM];
-  __shared__ float s_ds[2][kBtBM];
+struct BtTile {
+  BtGroup g;
+  int v, m0, n0, steps;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uni(tid >> 6), wm = wave >> 1, wn = wave & 1;
-  const int V = a.N + a.K_s;
-  for (int i = tid; i <= V; i += kBtThreads) s_tab[i] = tab[i];
-  __syncthreads();
-  const int total = s_tab[V];
-  if ((int)blockIdx.x >= total) return;
-  // slot-row products: consecutive tiles (m fastest: one weight tile, several
-  // token tiles) go to one XCD.  Weight-gradient products keep the launch
-  // order (longest tiles first); their m-tiles then fall on the XCDs in turn,
-  // and each XCD sees the same m-tile of every n-tile.
-  const int L = (G == BT_DWD || G == BT_DWGC) ? (int)blockIdx.x
-                                              : bt_xcd_swizzle(blockIdx.x, total);
+// Tile L of product G: its group (through the table's order), m-tile and n-tile.
+template <int G>
+__device__ __forceinline__ BtTile bt_tile_of(const BwdArgs& a, const int* s_tab, int V, int L) {
   int lo = 0, hi = V - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (s_tab[mid] <= L) lo = mid; else hi = mid - 1;
   }
-  const int k_tab = lo;
-  const int v = uni(bt_order<G>(a, lo));
-  const BtGroup g = bt_group<G>(a, v);
-  constexpr int BN = bt_bn(G);
-  const int nmt = (g.M + kBtBM - 1) / kBtBM;
-  const int local = L - s_tab[k_tab];
-  const int m0 = uni((local % nmt) * kBtBM), n0 = uni((local / nmt) * BN);
-  const int steps = uni(g.steps);
+  BtTile t;
+  t.v = uni(bt_order<G>(a, lo));
+  t.g = bt_group<G>(a, t.v);
+  t.g.M = uni(t.g.M);
+  t.g.Nc = uni(t.g.Nc);
+  t.g.rows = uni(t.g.rows);
+  t.g.base = uni(t.g.base);
+  const int nmt = (t.g.M + kBtBM - 1) / kBtBM;
+  const int local = L - s_tab[lo];
+  t.m0 = uni((local % nmt) * kBtBM);
+  t.n0 = uni((local / nmt) * bt_bn(G));
+  t.steps = uni(t.g.steps);
+  return t;
+}
 
-  if (G == BT_AC && tid < kBtBM) {
-    const int m = m0 + tid;
-    float gv = 0.f;  // rows past the expert's last slot contribute nothing
-    if (m < g.M) {
-      if (g.routed) {
+// This lane's direct-to-LDS rows of tile t (wavefronts 0-3 the A rows, 4-7 the B
+// rows): a wavefront-uniform base at k = 0 and 32-bit lane offsets.
+template <int G>
+__device__ __forceinline__ const uint8_t* bt_prepare(const BwdArgs& a, const BtTile& t, int wave,
+                                                     int lane, uint32_t (&off)[kBtNI]) {
+  const bool is_a = wave < 4;
+  constexpr bool gathered = G == BT_DP || G == BT_AC;
+  const uint8_t* b0 = is_a ? (gathered ? (const uint8_t*)(G == BT_DP ? a.dh : a.u)
+                                       : bt_a_row<G>(a, t.v, t.g, min(t.m0, t.g.M - 1)))
+                           : bt_b_row<G>(a, t.v, t.n0, 0);
+  const uint8_t* base = uni(b0);
+#pragma unroll
+  for (int i = 0; i < kBtNI; ++i) {
+    const int r = ((wave & 3) * kBtNI + i) * 8 + (lane >> 3);
+    const uint8_t* rp = is_a ? bt_a_row<G>(a, t.v, t.g, min(t.m0 + r, t.g.M - 1))
+                             : bt_b_row<G>(a, t.v, t.n0, r);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    off[i] = (uint32_t)(rp - base) + chunk * 16;
+  }
+  return base;
+}
+
+// AC: the gate of every tile row (rows past the expert's last slot: 0).
+__device__ __forceinline__ void bt_fill_gate(const BwdArgs& a, const BtTile& t, float* s_gate) {
+  const int tid = threadIdx.x;
+  if (tid < kBtBM) {
+    const int m = t.m0 + tid;
+    float gv = 0.f;
+    if (m < t.g.M) {
+      if (t.g.routed) {
         const int TK = a.T * a.K;
-        const int p = a.sorted_pair[g.base + m];
+        const int p = a.sorted_pair[t.g.base + m];
         gv = ((unsigned)p < (unsigned)TK) ? a.gate[p] : 0.f;
       } else {
         gv = 1.f;
@@ -420,54 +438,21 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
     }
     s_gate[tid] = gv;
   }
+}
 
-  // this lane's direct-to-LDS rows: wavefronts 0-3 the A rows, 4-7 the B rows
-  const bool is_a = wave < 4;
-  const uint8_t* base;
-  uint32_t off[kBtNI];
-  {
-    const bool gathered = G == BT_DP || G == BT_AC;
-    const uint8_t* b0 = is_a ? (gathered ? (const uint8_t*)(G == BT_DP ? a.dh : a.u)
-                                         : bt_a_row<G>(a, v, g, min(m0, g.M - 1)))
-                             : bt_b_row<G>(a, v, n0, 0);
-    base = uni(b0);
-#pragma unroll
-    for (int i = 0; i < kBtNI; ++i) {
-      const int r = ((wave & 3) * kBtNI + i) * 8 + (lane >> 3);
-      const uint8_t* rp = is_a ? bt_a_row<G>(a, v, g, min(m0 + r, g.M - 1)) : bt_b_row<G>(a, v, n0, r);
-      const int chunk = (lane & 7) ^ ((r >> 1) & 7);
-      off[i] = (uint32_t)(rp - base) + chunk * 16;
-    }
-  }
-  uint8_t* const w0 = lds0 + wave * kBtNI * 1024;
-  uint8_t* const w1 = lds1 + wave * kBtNI * 1024;
-
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  if (steps > 0) {
-#pragma unroll
-    for (int i = 0; i < kBtNI; ++i) dma16(base, off[i], w0 + i * 1024);
-  }
-  for (int s = 0; s < steps; ++s) {
-    pipe_sync();  // k-step s has landed; every wavefront is done with the other slot
-    const uint8_t* rd = (s & 1) ? lds1 : lds0;
-    uint8_t* wr = (s & 1) ? w0 : w1;
-    const bool more = s + 1 < steps;
-    bt_mma<G>(rd, wm, wn, lane, acc, uni(base + (size_t)(more ? s + 1 : 0) * kBtRB), off, wr,
-              more ? 0x7fffffff : 0);
-  }
-  pipe_sync();  // the ring is free for the epilogue (the zero loads have landed)
-
+// Epilogue of tile t.
+template <int G>
+__device__ __forceinline__ void bt_epilogue(const BwdArgs& a, const BtTile& t, int wm, int wn,
+                                            int lane, f32x16 (&acc)[2][4],
+                                            uint8_t* __restrict__ lds0, uint8_t* __restrict__ lds1,
+                                            const float* s_gate, float (*s_ds)[kBtBM]) {
+  const int tid = threadIdx.x;
+  const BtGroup& g = t.g;
+  const int v = t.v, m0 = t.m0, n0 = t.n0;
   // acc[fm][fn][r]: tile row wm*64 + fm*32 + 8(r/4) + 4(lane/32) + r%4,
   // tile column bt_bcol(wn, fn) + lane%32
   const int lc = lane & 31, lh = lane >> 5;
-  if (G != BT_AC) {
+  if constexpr (G != BT_AC) {
     const size_t Id = (size_t)a.I * a.d;
     const int j = v - a.N;
 #pragma unroll
@@ -619,6 +604,132 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
   bt_store_t(lds0, (uint16_t*)a.gPT, a.ldp, n0, cp, ncols, nch);
 }
 
+// Grouped k-major GEMM C = A B^T for product G (bfloat16 operands, float32
+// accumulation).  Persistent, one block per CU, 256 x bt_bn(G) tiles.
+// Slot-row products: each XCD (blocks are dealt to the XCDs round-robin)
+// owns a contiguous range of tiles (m fastest: the tiles of one weight tile
+// share an L2) and its blocks claim them from the range's counter.  Weight-
+// gradient products: one counter over the table's order (longest first).
+// After a tile's last k-step the next tile's first k-step is already loading
+// while the tile is written out (AC, whose epilogue stages through the ring,
+// loads it afterwards).
+template <int G>
+__global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
+                                                                const int32_t* __restrict__ tab,
+                                                                int32_t* __restrict__ counters) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBtSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBtSlot];
+  __shared__ int s_tab[kBtMaxV + 1];
+  __shared__ float s_gate[kBtBM];
+  __shared__ float s_ds[2][kBtBM];
+  __shared__ int s_claim[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6), wm = wave >> 1, wn = wave & 1;
+  const int V = a.N + a.K_s;
+  for (int i = tid; i <= V; i += kBtThreads) s_tab[i] = tab[i];
+  __syncthreads();
+  const int total = s_tab[V];
+  constexpr bool kWgrad = G == BT_DWD || G == BT_DWGC;
+  // AC keeps one tile per block: its staged epilogue needs every register
+  // the loop state would hold
+  constexpr bool kPersist = G != BT_AC;
+  int start, end, stride, x;
+  if (!kPersist) {
+    start = 0;
+    end = total;
+    stride = 0;
+    x = 0;
+  } else if (kWgrad) {
+    start = 0;
+    end = total;
+    stride = gridDim.x;
+    x = 0;
+  } else {
+    const int X = min(8, (int)gridDim.x);
+    x = blockIdx.x % X;
+    start = (int)((long long)total * x / X);
+    end = (int)((long long)total * (x + 1) / X);
+    stride = ((int)gridDim.x - x + X - 1) / X;
+  }
+  int L;
+  if (!kPersist) {
+    if ((int)blockIdx.x >= total) return;
+    L = bt_xcd_swizzle(blockIdx.x, total);
+  } else {
+    L = start + (kWgrad ? (int)blockIdx.x : (int)blockIdx.x / min(8, (int)gridDim.x));
+    if (L >= end) return;
+  }
+  int32_t* const ctr = counters + x;
+  const int claim_base = start + stride;
+
+  BtTile cur = bt_tile_of<G>(a, s_tab, V, L);
+  uint32_t off[kBtNI];
+  const uint8_t* base = bt_prepare<G>(a, cur, wave, lane, off);
+  if (G == BT_AC) bt_fill_gate(a, cur, s_gate);
+  int ph = 0;  // ring slot of the current tile's k-step 0
+  if (cur.steps > 0) {
+    uint8_t* w = lds0 + wave * kBtNI * 1024;
+#pragma unroll
+    for (int i = 0; i < kBtNI; ++i) dma16(base, off[i], w + i * 1024);
+  }
+  for (int it = 0;; ++it) {
+    if (kPersist && tid == 0) s_claim[it & 1] = claim_base + atomicAdd(ctr, 1);
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    int Ln = end;
+    BtTile nxt = cur;
+    bool pre = false;  // the next tile's first k-step was issued under this tile
+    if (kPersist && cur.steps == 0) {
+      // (the wait also lands the zero loads issued into this slot under the
+      // previous tile before the slot is loaded again)
+      pipe_sync();
+      Ln = uni(s_claim[it & 1]);
+      if (G != BT_AC && Ln < end) {
+        nxt = bt_tile_of<G>(a, s_tab, V, Ln);
+        base = bt_prepare<G>(a, nxt, wave, lane, off);
+        pre = true;
+        uint8_t* w = ((ph & 1) ? lds1 : lds0) + wave * kBtNI * 1024;
+#pragma unroll
+        for (int i = 0; i < kBtNI; ++i) dma16(base, off[i], w + i * 1024, nxt.steps > 0 ? 0x7fffffff : 0);
+      }
+    }
+    for (int s = 0; s < cur.steps; ++s) {
+      pipe_sync();  // k-step s has landed; every wavefront is done with the other slot
+      const int q = (ph + s) & 1;
+      const uint8_t* rd = q ? lds1 : lds0;
+      uint8_t* wr = (q ? lds0 : lds1) + wave * kBtNI * 1024;
+      const uint8_t* db = base + (size_t)(s + 1) * kBtRB;
+      int nrec = 0x7fffffff;
+      if (s + 1 == cur.steps) {
+        Ln = kPersist ? uni(s_claim[it & 1]) : end;
+        nrec = 0;
+        db = base;
+        if (G != BT_AC && Ln < end) {
+          nxt = bt_tile_of<G>(a, s_tab, V, Ln);
+          base = bt_prepare<G>(a, nxt, wave, lane, off);
+          db = base;
+          pre = true;
+          if (nxt.steps > 0) nrec = 0x7fffffff;
+        }
+      }
+      bt_mma<G>(rd, wm, wn, lane, acc, uni(db), off, wr, nrec);
+    }
+    if (G == BT_AC) pipe_sync();  // the ring is free for the staged epilogue
+    bt_epilogue<G>(a, cur, wm, wn, lane, acc, lds0, lds1, s_gate, s_ds);
+    ph += cur.steps;
+    // a persistent product always issued the next tile's first k-step above
+    if (!kPersist || Ln >= end || !pre) break;
+    cur = nxt;
+  }
+  MOE_WAIT_VMCNT(0);  // no direct-to-LDS load outlives the block
+}
+
 // ds_pair[p] = sum of the partial gate gradients of p's slot, in column order.
 __global__ __launch_bounds__(256) void bt_ds_kernel(const float* __restrict__ dsp, int NT,
                                                     const int32_t* __restrict__ slot_of, int TK,
@@ -644,18 +755,35 @@ long long bt_grid(int G, const BwdArgs& a) {
   }
 }
 
+int bt_cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      n = cus;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 template <int G>
-hipError_t bt_launch(const BwdArgs& a, const int32_t* tabs, hipStream_t st) {
-  const long long grid = bt_grid(G, a);
-  if (grid <= 0) return hipSuccess;
+hipError_t bt_launch(const BwdArgs& a, int32_t* tabs, hipStream_t st) {
+  const long long ub = bt_grid(G, a);
+  if (ub <= 0) return hipSuccess;
   const int V = a.N + a.K_s;
-  bt_gemm_kernel<G><<<dim3((unsigned)grid), dim3(kBtThreads), 0, st>>>(a, tabs + (G - 1) * (V + 1));
+  const long long grid = G == BT_AC ? ub : std::min<long long>(ub, bt_cu_count());
+  bt_gemm_kernel<G><<<dim3((unsigned)grid), dim3(kBtThreads), 0, st>>>(
+      a, tabs + (G - 1) * (V + 1), tabs + BT_NG * (V + 1) + (G - 1) * 8);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int bt_tables_ints(int N, int K_s) { return BT_NG * (N + K_s + 1); }
+// tile tables of the five products, then 8 claim counters per product
+int bt_tables_ints(int N, int K_s) { return BT_NG * (N + K_s + 1) + BT_NG * 8; }
 
 hipError_t launch_bt_prep(const BwdArgs& a, int32_t* tabs, hipStream_t st) {
   const int V = a.N + a.K_s;
@@ -670,7 +798,7 @@ hipError_t launch_bt_prep(const BwdArgs& a, int32_t* tabs, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bt_gemm(int G, const BwdArgs& a, const int32_t* tabs, hipStream_t st) {
+hipError_t launch_bt_gemm(int G, const BwdArgs& a, int32_t* tabs, hipStream_t st) {
   switch (G) {
     case BT_DP: return bt_launch<BT_DP>(a, tabs, st);
     case BT_AC: return bt_launch<BT_AC>(a, tabs, st);

@@ -166,7 +166,7 @@ inline long long bt_routed_cols(int T, int K, int N) {
 __host__ __device__ inline int bt_pad64(int x) { return (x + 63) & ~63; }
 int bt_tables_ints(int N, int K_s);
 hipError_t launch_bt_prep(const BwdArgs& a, int32_t* tabs, hipStream_t st);
-hipError_t launch_bt_gemm(int G, const BwdArgs& a, const int32_t* tabs, hipStream_t st);
+hipError_t launch_bt_gemm(int G, const BwdArgs& a, int32_t* tabs, hipStream_t st);
 hipError_t launch_bt_ds(const BwdArgs& a, const int32_t* slot_of, float* ds_pair, hipStream_t st);
 // tabs: the pipelined bfloat16 path's tables (bt_tables_ints + N + 1 ints for
 // the padded columns), or NULL for the generic path.
