@@ -19,6 +19,8 @@
 // ("k-major": rows of 64-byte k-steps, staged as they are) or contiguous
 // along the output dimension ("r-major": staged into LDS transposed); rows
 // gathered through the dispatch order where the operand is a token row.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -475,39 +477,61 @@ __device__ __forceinline__ void bw_store8(float* p, const float (&v)[8]) {
 }
 
 // du_t = dh_t + sum_k dX[slot_of(t, k)] + sum_j dXs[j][t] + E_gate^T dz_t, one
-// float32 sum in that order, rounded once.  One block per token, eight
-// columns per thread; the token's dz row is read once into LDS.
-template <class E>
+// float32 sum in that order, rounded once.  A block takes kDuTok tokens, a
+// thread eight columns of each (every E_gate chunk is read once for all of
+// them); the tokens' dz rows and slots are read once into LDS.  dX rows are
+// bfloat16 (XB) or float32.
+constexpr int kDuTok = 8;
+template <class E, bool XB>
 __global__ __launch_bounds__(256) void bw_du_kernel(BwdArgs a, const int32_t* __restrict__ slot_of,
                                                     const float* __restrict__ dz, void* du) {
   using Tp = typename E::T;
-  __shared__ float s_dz[256];
-  __shared__ int s_slot[256];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  for (int i = tid; i < a.N; i += 256) s_dz[i] = dz[(size_t)t * a.N + i];
-  for (int k = tid; k < a.K; k += 256) s_slot[k] = slot_of[(size_t)t * a.K + k];
+  using Xt = typename std::conditional<XB, uint16_t, float>::type;
+  __shared__ float s_dz[kDuTok][256];
+  __shared__ int s_slot[kDuTok][256];
+  const int t0 = blockIdx.x * kDuTok, tid = threadIdx.x;
+  const int nt = min(kDuTok, a.T - t0);
+  for (int q = tid; q < nt * a.N; q += 256) s_dz[q / a.N][q % a.N] = dz[(size_t)t0 * a.N + q];
+  for (int q = tid; q < nt * a.K; q += 256) s_slot[q / a.K][q % a.K] = slot_of[(size_t)t0 * a.K + q];
+  for (int q = nt * 256 + tid; q < kDuTok * 256; q += 256) s_dz[q / 256][q % 256] = 0.f;
   __syncthreads();
   const Tp* Eg = (const Tp*)a.E_gate;
+  const Xt* dX = (const Xt*)a.dX;
+  const Xt* dXs = (const Xt*)a.dXs;
   for (int n = tid * 8; n < a.d; n += 256 * 8) {
-    float acc[8], v[8];
-    bw_load8((const Tp*)a.dh + (size_t)t * a.d + n, acc);
-    for (int k = 0; k < a.K; ++k) {
-      bw_load8(a.dX + (size_t)s_slot[k] * a.d + n, v);
+    float acc[kDuTok][8], v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += v[e];
-    }
-    for (int j = 0; j < a.K_s; ++j) {
-      bw_load8(a.dXs + ((size_t)j * a.T + t) * a.d + n, v);
+    for (int tb = 0; tb < kDuTok; ++tb) {
+      if (tb >= nt) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+        for (int e = 0; e < 8; ++e) acc[tb][e] = 0.f;
+        continue;
+      }
+      const int t = t0 + tb;
+      bw_load8((const Tp*)a.dh + (size_t)t * a.d + n, acc[tb]);
+      for (int k = 0; k < a.K; ++k) {
+        bw_load8(dX + (size_t)s_slot[tb][k] * a.d + n, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[tb][e] += v[e];
+      }
+      for (int j = 0; j < a.K_s; ++j) {
+        bw_load8(dXs + ((size_t)j * a.T + t) * a.d + n, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[tb][e] += v[e];
+      }
     }
     for (int i = 0; i < a.N; ++i) {
-      const float z = s_dz[i];
       bw_load8(Eg + (size_t)i * a.d + n, v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += z * v[e];
+      for (int tb = 0; tb < kDuTok; ++tb) {
+        const float z = s_dz[tb][i];  // rows past the batch are never stored
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[tb][e] += z * v[e];
+      }
     }
-    bw_store8((Tp*)du + (size_t)t * a.d + n, acc);
+#pragma unroll
+    for (int tb = 0; tb < kDuTok; ++tb)
+      if (tb < nt) bw_store8((Tp*)du + (size_t)(t0 + tb) * a.d + n, acc[tb]);
   }
 }
 
@@ -590,7 +614,7 @@ hipError_t backward_t(const BwdArgs& a, const float* gate, const float* scores,
                                                           a.dE_gate);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  bw_du_kernel<E><<<a.T, 256, 0, st>>>(a, slot_of, dz, du);
+  bw_du_kernel<E, false><<<(a.T + kDuTok - 1) / kDuTok, 256, 0, st>>>(a, slot_of, dz, du);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (dgate_bias != nullptr) {
     bw_db_kernel<<<a.N, 256, 0, st>>>(dz, a.T, a.N, dgate_bias);
@@ -624,7 +648,7 @@ hipError_t backward_pipe_bf16(const BwdArgs& a, const float* scores, const int32
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = launch_bt_gemm(3, a, tabs, st)) != hipSuccess) return e;  // dx
-  bw_du_kernel<E><<<a.T, 256, 0, st>>>(a, slot_of, dz, du);
+  bw_du_kernel<E, true><<<(a.T + kDuTok - 1) / kDuTok, 256, 0, st>>>(a, slot_of, dz, du);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_bt_gemm(4, a, tabs, st)) != hipSuccess) return e;  // dW_down
   if ((e = launch_bt_gemm(5, a, tabs, st)) != hipSuccess) return e;  // dW_gate, dW_up

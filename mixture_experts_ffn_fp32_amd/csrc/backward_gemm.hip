@@ -18,7 +18,7 @@
 //        p = SiLU(a) c, da = g dP c SiLU'(a), dc = g dP SiLU(a),
 //        writes dAC (slot-major), dACT and (g p)^T (column-major), and the
 //        partial gate gradients sum_i dP p per 128 columns
-//   DX   dx[slot][n]   = dAC[slot] . WguT[n]              (K = 2I)
+//   DX   dx[slot][n]   = dAC[slot] . WguT[n]              (K = 2I), bfloat16 rows
 //   DWD  dW_down[n][i] = dhT[n] . gPT[i]                  (K = the expert's padded slots)
 //   DWGC dW_gu[j][n]   = dACT[j] . XT[n]                  (K = the same)
 // Padded slot columns hold zeros, so a contraction over them needs no mask.
@@ -336,7 +336,11 @@ __device__ __forceinline__ void bt_mma(const uint8_t* __restrict__ rd, int wm, i
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = bt_mfma(af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
+      for (int fn = 0; fn < 4; ++fn)
+        // DX: weights as the 32-row operand, so a lane holds four consecutive
+        // output columns of one slot row (8-byte bf16 stores)
+        acc[fm][fn] = G == BT_DX ? bt_mfma(bfr[kg & 1][fn], af[kg & 1][fm], acc[fm][fn])
+                                 : bt_mfma(af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
   }
   __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
@@ -452,7 +456,31 @@ __device__ __forceinline__ void bt_epilogue(const BwdArgs& a, const BtTile& t, i
   // acc[fm][fn][r]: tile row wm*64 + fm*32 + 8(r/4) + 4(lane/32) + r%4,
   // tile column bt_bcol(wn, fn) + lane%32
   const int lc = lane & 31, lh = lane >> 5;
-  if constexpr (G != BT_AC) {
+  if constexpr (G == BT_DX) {
+    // swapped operands: acc[fm][fn][4q + e] is slot row wm*64 + fm*32 + lane%32,
+    // column bt_bcol(wn, fn) + 8q + 4(lane/32) + e; dx rows go out as bfloat16
+    const int j = v - a.N;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+      const int m = m0 + wm * 64 + fm * 32 + lc;
+      if (m >= g.M) continue;
+      uint16_t* c = g.routed ? (uint16_t*)a.dX + (size_t)(g.base + m) * a.d
+                             : (uint16_t*)a.dXs + ((size_t)j * a.T + m) * a.d;
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + bt_bcol<G>(wn, fn) + 8 * q + 4 * lh;
+          if (n < g.Nc) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1]);
+            w.y = pack_bf16x2(acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]);
+            *(uint2*)(c + n) = w;
+          }
+        }
+    }
+    return;
+  } else if constexpr (G != BT_AC) {
     const size_t Id = (size_t)a.I * a.d;
     const int j = v - a.N;
 #pragma unroll
@@ -466,9 +494,6 @@ __device__ __forceinline__ void bt_epilogue(const BwdArgs& a, const BtTile& t, i
           case BT_DP:
             c = g.routed ? a.dP + (size_t)(g.base + m) * a.I
                          : a.dPs + ((size_t)m * a.K_s + j) * a.I;
-            break;
-          case BT_DX:
-            c = g.routed ? a.dX + (size_t)(g.base + m) * a.d : a.dXs + ((size_t)j * a.T + m) * a.d;
             break;
           case BT_DWD:
             c = (g.routed ? a.dW_routed + (size_t)v * 3 * Id : a.dW_shared + (size_t)j * 3 * Id) +
