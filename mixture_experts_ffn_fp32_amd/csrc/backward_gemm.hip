@@ -2,23 +2,24 @@
 // summary, papercache.org, sec. 3.2 layer equation, differentiated by the
 // chain rule with each token's top-K set held fixed).
 //
-// Every expert-slot product of the backward runs as a grouped GEMM whose two
-// operands are contiguous along the contraction ("k-major"), so all of them
-// share one LDS-DMA MFMA pipeline: tiles of 256 x 256, eight wavefronts of
-// 64 x 128, 128-byte k-steps landing by direct-to-LDS loads in a two-slot ring
-// while the other slot is multiplied.  Operands that are naturally laid out
-// along the output dimension are transposed once beforehand:
+// Every expert-slot product of the backward runs as a grouped GEMM on one
+// LDS-DMA MFMA pipeline: tiles of 256 x 256, eight wavefronts of 64 x 128,
+// k-steps landing by direct-to-LDS loads in a two-slot ring while the other
+// slot is multiplied.  The A operand is always contiguous along the
+// contraction ("k-major"); the weights of DP and DX are read in their stored
+// layout (rows along the contraction) and turned into MFMA fragments by
+// transposing LDS reads; the weight-gradient products contract over slots,
+// whose operands are transposed once beforehand:
 //
-//   WdT  = W_down^T, WguT = [W_gate; W_up]^T             (per virtual expert)
 //   XT, dhT = u^T, dh^T over padded slot columns          (gathered by dispatch)
 //
 // Products, per virtual expert v (routed: its slots; shared: every token):
-//   DP   dP[slot][i]   = dh_tok . WdT[i]                  (K = d)
+//   DP   dP[slot][i]   = dh_tok . W_down[:, i]            (K = d)
 //   AC   [a c][slot][i] = u_tok . [W_gate; W_up][i]        (K = d), fused epilogue:
 //        p = SiLU(a) c, da = g dP c SiLU'(a), dc = g dP SiLU(a),
 //        writes dAC (slot-major), dACT and (g p)^T (column-major), and the
 //        partial gate gradients sum_i dP p per 128 columns
-//   DX   dx[slot][n]   = dAC[slot] . WguT[n]              (K = 2I), bfloat16 rows
+//   DX   dx[slot][n]   = dAC[slot] . [W_gate; W_up][:, n]  (K = 2I), bfloat16 rows
 //   DWD  dW_down[n][i] = dhT[n] . gPT[i]                  (K = the expert's padded slots)
 //   DWGC dW_gu[j][n]   = dACT[j] . XT[n]                  (K = the same)
 // Padded slot columns hold zeros, so a contraction over them needs no mask.
@@ -144,77 +145,49 @@ __global__ __launch_bounds__(64) void bt_table_kernel(BwdArgs a, int32_t* __rest
 }
 
 // ---------------------------------------------------------------- transposes
-// Out[c][r] = In_r[c] over 64 x 64 tiles (bfloat16), through LDS.
-//  MODE 0: W_down^T per virtual expert (In rows n < d of I columns; z = v)
-//  MODE 1: [W_gate; W_up]^T            (In rows j < 2I of d columns; z = v)
-//  MODE 2: u^T (z = 0) and dh^T (z = 1) over the padded slot columns; row r
-//          is the token of padded column r, zero in the padding.
-template <int MODE>
-__global__ __launch_bounds__(256) void bt_transpose_kernel(BwdArgs a) {
+// u^T (z = 0) and dh^T (z = 1) over the padded slot columns, 64 x 64 tiles
+// through LDS: out[n][r] = the token row of padded column r at column n, zero
+// in the padding.
+__global__ __launch_bounds__(256) void bt_gather_t_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, z = blockIdx.z;
-  const size_t Id = (size_t)a.I * a.d;
-  const uint16_t* src = nullptr;  // row r0 of the input (MODE 0, 1)
-  size_t src_ld = 0;
-  uint16_t* dst;
-  size_t dst_ld;
-  // MODE 2: the virtual range this 64-column block lies in
-  int rv_lo = 0, rv_rows = 0, rv_slot0 = 0;
+  // the virtual range this 64-column block lies in
+  int rv_lo, rv_rows, rv_slot0 = 0;
   bool rv_routed = false;
-  if (MODE < 2) {
-    const uint16_t* W = z < a.N ? (const uint16_t*)a.W_routed + (size_t)z * 3 * Id
-                                : (const uint16_t*)a.W_shared + (size_t)(z - a.N) * 3 * Id;
-    if (MODE == 0) {
-      src = W + 2 * Id;
-      src_ld = a.I;
-      dst = (uint16_t*)a.WdT + (size_t)z * Id;
-      dst_ld = a.d;
-    } else {
-      src = W;
-      src_ld = a.d;
-      dst = (uint16_t*)a.WguT + (size_t)z * 2 * Id;
-      dst_ld = 2 * (size_t)a.I;
-    }
+  const int R = a.pcol[a.N];
+  if (r0 >= R + a.Tp) return;
+  if (r0 >= R) {
+    rv_lo = R;
+    rv_rows = a.T;
   } else {
-    const int R = a.pcol[a.N];
-    if (r0 >= R + a.Tp) return;
-    if (r0 >= R) {
-      rv_lo = R;
-      rv_rows = a.T;
-    } else {
-      int lo = 0, hi = a.N - 1;  // last routed expert whose range starts at or before r0
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.pcol[mid] <= r0) lo = mid; else hi = mid - 1;
-      }
-      const int TK = a.T * a.K;
-      rv_routed = true;
-      rv_lo = a.pcol[lo];
-      rv_slot0 = min(max(a.offsets[lo], 0), TK);
-      rv_rows = min(max(a.offsets[lo + 1], rv_slot0), TK) - rv_slot0;
+    int lo = 0, hi = a.N - 1;  // last routed expert whose range starts at or before r0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.pcol[mid] <= r0) lo = mid; else hi = mid - 1;
     }
-    dst = (uint16_t*)(z == 0 ? a.XT : a.dhT);
-    dst_ld = (size_t)a.ldx;
+    const int TK = a.T * a.K;
+    rv_routed = true;
+    rv_lo = a.pcol[lo];
+    rv_slot0 = min(max(a.offsets[lo], 0), TK);
+    rv_rows = min(max(a.offsets[lo + 1], rv_slot0), TK) - rv_slot0;
   }
+  uint16_t* dst = (uint16_t*)(z == 0 ? a.XT : a.dhT);
+  const size_t dst_ld = (size_t)a.ldx;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int q = tid + h * 256, r = q >> 3, ch = q & 7;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (MODE < 2) {
-      v = *(const u32x4*)(src + (size_t)(r0 + r) * src_ld + c0 + ch * 8);
-    } else {
-      const int local = r0 + r - rv_lo;
-      if (local < rv_rows) {
-        int tok = local;
-        if (rv_routed) {
-          const int TK = a.T * a.K;
-          const int p = a.sorted_pair[rv_slot0 + local];
-          tok = ((unsigned)p < (unsigned)TK) ? p / a.K : 0;
-        }
-        const uint16_t* row = (const uint16_t*)(z == 0 ? a.u : a.dh) + (size_t)tok * a.d;
-        v = *(const u32x4*)(row + c0 + ch * 8);
+    const int local = r0 + r - rv_lo;
+    if (local < rv_rows) {
+      int tok = local;
+      if (rv_routed) {
+        const int TK = a.T * a.K;
+        const int p = a.sorted_pair[rv_slot0 + local];
+        tok = ((unsigned)p < (unsigned)TK) ? p / a.K : 0;
       }
+      const uint16_t* row = (const uint16_t*)(z == 0 ? a.u : a.dh) + (size_t)tok * a.d;
+      v = *(const u32x4*)(row + c0 + ch * 8);
     }
     *(u32x4*)&tile[r][ch * 8] = v;
   }
@@ -263,9 +236,6 @@ template <int G>
 __device__ __forceinline__ const uint8_t* bt_b_row(const BwdArgs& a, int v, int n0, int r) {
   const size_t Id = (size_t)a.I * a.d;
   switch (G) {
-    case BT_DP:
-      return (const uint8_t*)((const uint16_t*)a.WdT + (size_t)v * Id +
-                              (size_t)min(n0 + r, a.I - 1) * a.d);
     case BT_AC: {
       const uint16_t* W = v < a.N ? (const uint16_t*)a.W_routed + (size_t)v * 3 * Id
                                   : (const uint16_t*)a.W_shared + (size_t)(v - a.N) * 3 * Id;
@@ -275,9 +245,6 @@ __device__ __forceinline__ const uint8_t* bt_b_row(const BwdArgs& a, int v, int 
       const int i = r < half ? min(n0 + r, a.I - 1) : a.I + min(n0 + r - half, a.I - 1);
       return (const uint8_t*)(W + (size_t)i * a.d);
     }
-    case BT_DX:
-      return (const uint8_t*)((const uint16_t*)a.WguT + (size_t)v * 2 * Id +
-                              (size_t)min(n0 + r, a.d - 1) * 2 * a.I);
     case BT_DWD:
       return (const uint8_t*)((const uint16_t*)a.gPT + (size_t)min(n0 + r, a.I - 1) * a.ldp +
                               bt_colp(a, v));
@@ -295,6 +262,41 @@ __device__ __forceinline__ int bt_bcol(int wn, int fn) {
   return (wn * 4 + fn) * 32;
 }
 
+// DP and DX read their B operand (W_down, [W_gate; W_up]) in its stored
+// layout, rows along the contraction: the B tile of a k-step is 64 rows of
+// 256 output columns (512 bytes, 16-byte chunk c of row k at c ^ 2(k & 7)),
+// and the MFMA fragments come out of LDS through transposing reads.
+__host__ __device__ constexpr bool bt_btr(int G) { return G == BT_DP || G == BT_DX; }
+
+__device__ __forceinline__ int bt_btr_off(int k, int n) {
+  return kBtBM * kBtRB + k * 512 + ((((n >> 3) ^ ((k & 7) << 1))) << 4) + (n & 7) * 2;
+}
+
+// Row 0 of the stored B operand of DP / DX, its row pitch and width (elements).
+template <int G>
+__device__ __forceinline__ const uint16_t* bt_btr_src(const BwdArgs& a, int v, int& pitch,
+                                                      int& width) {
+  const size_t Id = (size_t)a.I * a.d;
+  const uint16_t* W = v < a.N ? (const uint16_t*)a.W_routed + (size_t)v * 3 * Id
+                              : (const uint16_t*)a.W_shared + (size_t)(v - a.N) * 3 * Id;
+  if (G == BT_DP) {  // W_down [d][I]: row n, columns i
+    pitch = width = a.I;
+    return W + 2 * Id;
+  }
+  pitch = width = a.d;  // [W_gate; W_up] [2I][d]: row j, columns n
+  return W;
+}
+
+// Four consecutive contraction indices of one column through a transposing
+// LDS read: within each 16-lane group, lane j names row (k0 + j / 4) at column
+// (n0 + 4 (j % 4)), and lane i receives column n0 + i of rows k0 .. k0 + 3.
+typedef short bt_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 bt_read_tr(const uint8_t* p) {
+  const bt_v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) bt_v4s*)(__attribute__((address_space(3))) const uint8_t*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
 __device__ __forceinline__ f32x16 bt_mfma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -307,9 +309,23 @@ __device__ __forceinline__ void bt_frags(const uint8_t* __restrict__ rd, int kg,
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
     af[fm] = *(const u32x4*)(rd + lds_chunk_offset(wm * 64 + fm * 32 + (lane & 31), ch));
+  if constexpr (bt_btr(G)) {
+    // lane l: column 16((l / 16) % 2) + 4(l % 4) of the fragment names rows
+    // kg*16 + 8(l / 32) + (l % 16) / 4 (+ 4 for the upper half of the 8 k values)
+    const int k = kg * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int nl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-  for (int fn = 0; fn < 4; ++fn)
-    bfr[fn] = *(const u32x4*)(rd + lds_chunk_offset(kBtBM + bt_bcol<G>(wn, fn) + (lane & 31), ch));
+    for (int fn = 0; fn < 4; ++fn) {
+      const int n = bt_bcol<G>(wn, fn) + nl;
+      const uint2 lo = bt_read_tr(rd + bt_btr_off(k, n));
+      const uint2 hi = bt_read_tr(rd + bt_btr_off(k + 4, n));
+      bfr[fn] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  } else {
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+      bfr[fn] = *(const u32x4*)(rd + lds_chunk_offset(kBtBM + bt_bcol<G>(wn, fn) + (lane & 31), ch));
+  }
 }
 
 // One k-step out of ring slot `rd`.  The next k-step's direct-to-LDS loads
@@ -342,14 +358,18 @@ __device__ __forceinline__ void bt_mma(const uint8_t* __restrict__ rd, int wm, i
         acc[fm][fn] = G == BT_DX ? bt_mfma(bfr[kg & 1][fn], af[kg & 1][fm], acc[fm][fn])
                                  : bt_mfma(af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  constexpr int NR = bt_btr(G) ? 2 + 8 : 2 + 4;  // LDS reads per k-group
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
   for (int kg = 0; kg < KG; ++kg) {
-    const int nr = kg + 1 < KG ? 6 : 0, nd = (ISSUE && kg < PARTS) ? PER : 0;
+    const int nr = kg + 1 < KG ? NR : 0, nd = (ISSUE && kg < PARTS) ? PER : 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (m < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (m < nr) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (NR > 8 && m < NR - 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       if (m < nd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   }
@@ -407,20 +427,42 @@ __device__ __forceinline__ BtTile bt_tile_of(const BwdArgs& a, const int* s_tab,
 // rows): a wavefront-uniform base at k = 0 and 32-bit lane offsets.
 template <int G>
 __device__ __forceinline__ const uint8_t* bt_prepare(const BwdArgs& a, const BtTile& t, int wave,
-                                                     int lane, uint32_t (&off)[kBtNI]) {
-  const bool is_a = wave < 4;
-  constexpr bool gathered = G == BT_DP || G == BT_AC;
-  const uint8_t* b0 = is_a ? (gathered ? (const uint8_t*)(G == BT_DP ? a.dh : a.u)
-                                       : bt_a_row<G>(a, t.v, t.g, min(t.m0, t.g.M - 1)))
-                           : bt_b_row<G>(a, t.v, t.n0, 0);
-  const uint8_t* base = uni(b0);
+                                                     int lane, uint32_t (&off)[kBtNI],
+                                                     uint32_t& step) {
+  step = kBtRB;
+  const uint8_t* base;
+  if (wave < 4) {  // A rows
+    constexpr bool gathered = G == BT_DP || G == BT_AC;
+    base = uni(gathered ? (const uint8_t*)(G == BT_DP ? a.dh : a.u)
+                        : bt_a_row<G>(a, t.v, t.g, min(t.m0, t.g.M - 1)));
 #pragma unroll
-  for (int i = 0; i < kBtNI; ++i) {
-    const int r = ((wave & 3) * kBtNI + i) * 8 + (lane >> 3);
-    const uint8_t* rp = is_a ? bt_a_row<G>(a, t.v, t.g, min(t.m0 + r, t.g.M - 1))
-                             : bt_b_row<G>(a, t.v, t.n0, r);
-    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
-    off[i] = (uint32_t)(rp - base) + chunk * 16;
+    for (int i = 0; i < kBtNI; ++i) {
+      const int r = (wave * kBtNI + i) * 8 + (lane >> 3);
+      const uint8_t* rp = bt_a_row<G>(a, t.v, t.g, min(t.m0 + r, t.g.M - 1));
+      off[i] = (uint32_t)(rp - base) + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+    }
+  } else if constexpr (bt_btr(G)) {
+    // stored-layout B: instruction i of B wavefront w moves rows 2(8w + i) and
+    // 2(8w + i) + 1 of the k-step; lane L the chunk at position L % 32
+    int pitch, width;
+    base = uni((const uint8_t*)bt_btr_src<G>(a, t.v, pitch, width));
+    step = uni((int)(64 * pitch * 2));
+#pragma unroll
+    for (int i = 0; i < kBtNI; ++i) {
+      const int k = 2 * ((wave - 4) * kBtNI + i) + (lane >> 5);
+      const int c = (lane & 31) ^ ((k & 7) << 1);
+      // columns past the last one (a partial n-tile) reread the last chunk
+      const int col = min(t.n0 + 8 * c, width - 8);
+      off[i] = (uint32_t)(((size_t)k * pitch + col) * 2);
+    }
+  } else {  // B rows, contiguous along the contraction
+    base = uni(bt_b_row<G>(a, t.v, t.n0, 0));
+#pragma unroll
+    for (int i = 0; i < kBtNI; ++i) {
+      const int r = ((wave - 4) * kBtNI + i) * 8 + (lane >> 3);
+      const uint8_t* rp = bt_b_row<G>(a, t.v, t.n0, r);
+      off[i] = (uint32_t)(rp - base) + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+    }
   }
   return base;
 }
@@ -689,8 +731,8 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
   const int claim_base = start + stride;
 
   BtTile cur = bt_tile_of<G>(a, s_tab, V, L);
-  uint32_t off[kBtNI];
-  const uint8_t* base = bt_prepare<G>(a, cur, wave, lane, off);
+  uint32_t off[kBtNI], step;
+  const uint8_t* base = bt_prepare<G>(a, cur, wave, lane, off, step);
   if (G == BT_AC) bt_fill_gate(a, cur, s_gate);
   int ph = 0;  // ring slot of the current tile's k-step 0
   if (cur.steps > 0) {
@@ -717,7 +759,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
       Ln = uni(s_claim[it & 1]);
       if (G != BT_AC && Ln < end) {
         nxt = bt_tile_of<G>(a, s_tab, V, Ln);
-        base = bt_prepare<G>(a, nxt, wave, lane, off);
+        base = bt_prepare<G>(a, nxt, wave, lane, off, step);
         pre = true;
         uint8_t* w = ((ph & 1) ? lds1 : lds0) + wave * kBtNI * 1024;
 #pragma unroll
@@ -729,7 +771,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
       const int q = (ph + s) & 1;
       const uint8_t* rd = q ? lds1 : lds0;
       uint8_t* wr = (q ? lds0 : lds1) + wave * kBtNI * 1024;
-      const uint8_t* db = base + (size_t)(s + 1) * kBtRB;
+      const uint8_t* db = base + (size_t)(s + 1) * step;
       int nrec = 0x7fffffff;
       if (s + 1 == cur.steps) {
         Ln = kPersist ? uni(s_claim[it & 1]) : end;
@@ -737,7 +779,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
         db = base;
         if (G != BT_AC && Ln < end) {
           nxt = bt_tile_of<G>(a, s_tab, V, Ln);
-          base = bt_prepare<G>(a, nxt, wave, lane, off);
+          base = bt_prepare<G>(a, nxt, wave, lane, off, step);
           db = base;
           pre = true;
           if (nxt.steps > 0) nrec = 0x7fffffff;
@@ -811,15 +853,10 @@ hipError_t bt_launch(const BwdArgs& a, int32_t* tabs, hipStream_t st) {
 int bt_tables_ints(int N, int K_s) { return BT_NG * (N + K_s + 1) + BT_NG * 8; }
 
 hipError_t launch_bt_prep(const BwdArgs& a, int32_t* tabs, hipStream_t st) {
-  const int V = a.N + a.K_s;
   bt_table_kernel<<<1, 64, 0, st>>>(a, tabs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bt_transpose_kernel<0><<<dim3(a.I / 64, a.d / 64, V), 256, 0, st>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  bt_transpose_kernel<1><<<dim3(a.d / 64, 2 * a.I / 64, V), 256, 0, st>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  bt_transpose_kernel<2><<<dim3(a.d / 64, (unsigned)(a.ldx / 64), 2), 256, 0, st>>>(a);
+  bt_gather_t_kernel<<<dim3(a.d / 64, (unsigned)(a.ldx / 64), 2), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

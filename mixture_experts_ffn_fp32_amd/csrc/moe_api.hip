@@ -425,7 +425,7 @@ struct BwdLayout {
       tab, total;
   // pipelined bfloat16 path
   bool pipe;
-  size_t WdT, WguT, XT, dhT, dACT, gPT, dsp, tabs;
+  size_t XT, dhT, dACT, gPT, dsp, tabs;
   long long ldx, ldp;
 };
 
@@ -477,12 +477,9 @@ BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype)
   L.slot_of = take(TK * 4);
   L.tab = take((size_t)(std::max(N + K_s, moe::backward_de_chunks(T)) + 1) * 4);
   if (L.pipe) {
-    const size_t V = (size_t)N + K_s, Id = (size_t)I * d;
     const long long R = moe::bt_routed_cols(T, K, N), Tp = moe::bt_pad64(T);
     L.ldx = R + Tp;
     L.ldp = R + (long long)K_s * Tp;
-    L.WdT = take(V * Id * 2);
-    L.WguT = take(V * 2 * Id * 2);
     L.XT = take((size_t)d * L.ldx * 2);
     L.dhT = take((size_t)d * L.ldx * 2);
     L.dACT = take((size_t)2 * I * L.ldp * 2);
@@ -588,8 +585,6 @@ moe_status_t moe_layer_backward(const void* u, const void* E_gate, const void* W
   int32_t* tabs = nullptr;
   if (L.pipe) {
     tabs = (int32_t*)(ws + L.tabs);
-    a.WdT = ws + L.WdT;
-    a.WguT = ws + L.WguT;
     a.XT = ws + L.XT;
     a.dhT = ws + L.dhT;
     a.dACT = ws + L.dACT;

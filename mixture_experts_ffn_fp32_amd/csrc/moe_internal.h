@@ -145,10 +145,8 @@ struct BwdArgs {
   float* dW_routed;            // N weight blocks (float32)
   float* dW_shared;            // K_s weight blocks (float32)
   int T, d, I, N, K, K_s, NP;
-  // bfloat16 path (every product a k-major grouped GEMM on the LDS-DMA pipeline)
+  // bfloat16 path (every product a grouped GEMM on the LDS-DMA pipeline; V = N + K_s)
   const float* gate;           // [T*K] kept gates by pair
-  void* WdT;                   // [V][I][d]   W_down^T per virtual expert (V = N + K_s)
-  void* WguT;                  // [V][d][2I]  [W_gate; W_up]^T
   void* XT;                    // [d][ldx]    u^T over the padded slot columns
   void* dhT;                   // [d][ldx]    dh^T over the same columns
   void* dACT;                  // [2I][ldp]   [da, dc]^T over the padded slot columns
