@@ -5,24 +5,27 @@
 // Every expert-slot product of the backward runs as a grouped GEMM on one
 // LDS-DMA MFMA pipeline: tiles of 256 x 256, eight wavefronts of 64 x 128,
 // k-steps landing by direct-to-LDS loads in a two-slot ring while the other
-// slot is multiplied.  The A operand is always contiguous along the
-// contraction ("k-major"); the weights of DP and DX are read in their stored
-// layout (rows along the contraction) and turned into MFMA fragments by
-// transposing LDS reads; the weight-gradient products contract over slots,
-// whose operands are transposed once beforehand:
+// slot is multiplied.  An operand is either contiguous along the contraction
+// ("k-major": 256 rows of 128 bytes per k-step) or read in its stored layout
+// with rows along the contraction (64 rows of 256 columns per k-step; MFMA
+// fragments through transposing LDS reads).  Only the token rows that a
+// weight-gradient product contracts over are transposed beforehand:
 //
-//   XT, dhT = u^T, dh^T over padded slot columns          (gathered by dispatch)
+//   XT, dhT = u^T, dh^T over padded slot columns (gathered by dispatch, each
+//   expert's slots rounded up to 64, zeros in the padding)
 //
 // Products, per virtual expert v (routed: its slots; shared: every token):
-//   DP   dP[slot][i]   = dh_tok . W_down[:, i]            (K = d)
-//   AC   [a c][slot][i] = u_tok . [W_gate; W_up][i]        (K = d), fused epilogue:
-//        p = SiLU(a) c, da = g dP c SiLU'(a), dc = g dP SiLU(a),
-//        writes dAC (slot-major), dACT and (g p)^T (column-major), and the
-//        partial gate gradients sum_i dP p per 128 columns
-//   DX   dx[slot][n]   = dAC[slot] . [W_gate; W_up][:, n]  (K = 2I), bfloat16 rows
-//   DWD  dW_down[n][i] = dhT[n] . gPT[i]                  (K = the expert's padded slots)
-//   DWGC dW_gu[j][n]   = dACT[j] . XT[n]                  (K = the same)
-// Padded slot columns hold zeros, so a contraction over them needs no mask.
+//   DP   dP[slot][i]   = dh_tok . W_down[:, i]             (K = d)
+//   AC   [a c][slot][i] = u_tok . [W_gate; W_up][i]         (K = d), fused epilogue:
+//        p = SiLU(a) c, da = g dP c SiLU'(a), dc = g dP SiLU(a); writes
+//        [da dc] and g p slot-major, and the partial gate gradients
+//        sum_i dP p per 128 columns
+//   DX   dx[slot][n]   = [da dc][slot] . [W_gate; W_up][:, n] (K = 2I), bfloat16 rows
+//   DWD  dW_down[n][i] = dhT[n] . (g p)[:, i]              (K = the expert's slots)
+//   DWGC dW_gu[j][n]   = [da dc][:, j] . XT[n]             (K = the same)
+// Slot-major operands of the weight gradients stop at the expert's last slot
+// by a bounded buffer range (the loads past it return zeros); XT and dhT
+// hold zeros there.
 #include <algorithm>
 
 #include "lds_dma.h"
@@ -82,10 +85,6 @@ __device__ __forceinline__ int bt_tiles(const BwdArgs& a, int v) {
 // First padded column of virtual expert v in XT / dhT (shared experts share one range).
 __device__ __forceinline__ long long bt_colx(const BwdArgs& a, int v) {
   return v < a.N ? a.pcol[v] : a.pcol[a.N];
-}
-// ... and in dACT / gPT (one range per shared expert).
-__device__ __forceinline__ long long bt_colp(const BwdArgs& a, int v) {
-  return v < a.N ? a.pcol[v] : a.pcol[a.N] + (long long)(v - a.N) * a.Tp;
 }
 
 // Group order of product G's tile table.  The weight-gradient products
@@ -225,10 +224,8 @@ __device__ __forceinline__ const uint8_t* bt_a_row(const BwdArgs& a, int v, cons
       return (const uint8_t*)(g.routed
                                   ? (const uint16_t*)a.dAC + (size_t)(g.base + m) * 2 * a.I
                                   : (const uint16_t*)a.dACs + ((size_t)m * a.K_s + j) * 2 * a.I);
-    case BT_DWD:
+    default:  // BT_DWD (DWGC reads dAC in its stored layout)
       return (const uint8_t*)((const uint16_t*)a.dhT + (size_t)m * a.ldx + bt_colx(a, v));
-    default:
-      return (const uint8_t*)((const uint16_t*)a.dACT + (size_t)m * a.ldp + bt_colp(a, v));
   }
 }
 
@@ -245,10 +242,7 @@ __device__ __forceinline__ const uint8_t* bt_b_row(const BwdArgs& a, int v, int 
       const int i = r < half ? min(n0 + r, a.I - 1) : a.I + min(n0 + r - half, a.I - 1);
       return (const uint8_t*)(W + (size_t)i * a.d);
     }
-    case BT_DWD:
-      return (const uint8_t*)((const uint16_t*)a.gPT + (size_t)min(n0 + r, a.I - 1) * a.ldp +
-                              bt_colp(a, v));
-    default:
+    default:  // BT_DWGC (DWD reads g p in its stored layout)
       return (const uint8_t*)((const uint16_t*)a.XT + (size_t)min(n0 + r, a.d - 1) * a.ldx +
                               bt_colx(a, v));
   }
@@ -262,23 +256,44 @@ __device__ __forceinline__ int bt_bcol(int wn, int fn) {
   return (wn * 4 + fn) * 32;
 }
 
-// DP and DX read their B operand (W_down, [W_gate; W_up]) in its stored
-// layout, rows along the contraction: the B tile of a k-step is 64 rows of
-// 256 output columns (512 bytes, 16-byte chunk c of row k at c ^ 2(k & 7)),
-// and the MFMA fragments come out of LDS through transposing reads.
-__host__ __device__ constexpr bool bt_btr(int G) { return G == BT_DP || G == BT_DX; }
-
-__device__ __forceinline__ int bt_btr_off(int k, int n) {
-  return kBtBM * kBtRB + k * 512 + ((((n >> 3) ^ ((k & 7) << 1))) << 4) + (n & 7) * 2;
+// Operands read in their stored layout (rows along the contraction): the
+// tile of a k-step is 64 rows of 256 columns (512 bytes, 16-byte chunk c of
+// row k at c ^ 2(k & 7)) in the operand's half of the ring slot.
+//   A: DWGC's [da dc] (slot-major)
+//   B: DP's W_down, DX's [W_gate; W_up], DWD's g p (slot-major)
+__host__ __device__ constexpr bool bt_atr(int G) { return G == BT_DWGC; }
+__host__ __device__ constexpr bool bt_btr(int G) {
+  return G == BT_DP || G == BT_DX || G == BT_DWD;
 }
 
-// Row 0 of the stored B operand of DP / DX, its row pitch and width (elements).
+__device__ __forceinline__ int bt_tr_off(int region, int k, int n) {
+  return region + k * 512 + ((((n >> 3) ^ ((k & 7) << 1))) << 4) + (n & 7) * 2;
+}
+
+// Row 0 (contraction index 0) of a stored-layout operand of tile t, its row
+// pitch and width (elements), and the number of contraction rows that exist
+// (-1: all; a slot-major operand ends at the expert's last slot).
 template <int G>
-__device__ __forceinline__ const uint16_t* bt_btr_src(const BwdArgs& a, int v, int& pitch,
-                                                      int& width) {
+__device__ __forceinline__ const uint16_t* bt_tr_src(const BwdArgs& a, int v, const BtGroup& g,
+                                                     int& pitch, int& width, int& rows) {
   const size_t Id = (size_t)a.I * a.d;
+  const int j = v - a.N;
+  rows = -1;
+  if (G == BT_DWD) {  // g p [slot][I]
+    rows = g.rows;
+    width = a.I;
+    pitch = g.routed ? a.I : a.K_s * a.I;
+    return g.routed ? (const uint16_t*)a.P + (size_t)g.base * a.I : (const uint16_t*)a.Ps + (size_t)j * a.I;
+  }
+  if (G == BT_DWGC) {  // [da dc] [slot][2I]
+    rows = g.rows;
+    width = 2 * a.I;
+    pitch = g.routed ? 2 * a.I : a.K_s * 2 * a.I;
+    return g.routed ? (const uint16_t*)a.dAC + (size_t)g.base * 2 * a.I
+                    : (const uint16_t*)a.dACs + (size_t)j * 2 * a.I;
+  }
   const uint16_t* W = v < a.N ? (const uint16_t*)a.W_routed + (size_t)v * 3 * Id
-                              : (const uint16_t*)a.W_shared + (size_t)(v - a.N) * 3 * Id;
+                              : (const uint16_t*)a.W_shared + (size_t)j * 3 * Id;
   if (G == BT_DP) {  // W_down [d][I]: row n, columns i
     pitch = width = a.I;
     return W + 2 * Id;
@@ -297,9 +312,24 @@ __device__ __forceinline__ uint2 bt_read_tr(const uint8_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+__host__ __device__ constexpr bool bt_swap(int G) { return G == BT_AC || G == BT_DX; }
+
 __device__ __forceinline__ f32x16 bt_mfma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// MFMA fragments of k-group kg: 32 rows x 16 contraction indices, 8 per lane
+// (lane l: row l % 32, indices 8(l / 32) ..).  Stored-layout operands: within
+// each 16-lane group lane l names row kg*16 + 8(l / 32) + (l % 16) / 4 (+ 4 for
+// the upper four) at column 16((l / 16) % 2) + 4(l % 4) of the fragment.
+__device__ __forceinline__ u32x4 bt_frag_tr(const uint8_t* rd, int region, int kg, int col0,
+                                            int lane) {
+  const int k = kg * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int n = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const uint2 lo = bt_read_tr(rd + bt_tr_off(region, k, n));
+  const uint2 hi = bt_read_tr(rd + bt_tr_off(region, k + 4, n));
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
 template <int G>
@@ -308,24 +338,12 @@ __device__ __forceinline__ void bt_frags(const uint8_t* __restrict__ rd, int kg,
   const int ch = kg * 2 + (lane >> 5);
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
-    af[fm] = *(const u32x4*)(rd + lds_chunk_offset(wm * 64 + fm * 32 + (lane & 31), ch));
-  if constexpr (bt_btr(G)) {
-    // lane l: column 16((l / 16) % 2) + 4(l % 4) of the fragment names rows
-    // kg*16 + 8(l / 32) + (l % 16) / 4 (+ 4 for the upper half of the 8 k values)
-    const int k = kg * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
-    const int nl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    af[fm] = bt_atr(G) ? bt_frag_tr(rd, 0, kg, wm * 64 + fm * 32, lane)
+                       : *(const u32x4*)(rd + lds_chunk_offset(wm * 64 + fm * 32 + (lane & 31), ch));
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn) {
-      const int n = bt_bcol<G>(wn, fn) + nl;
-      const uint2 lo = bt_read_tr(rd + bt_btr_off(k, n));
-      const uint2 hi = bt_read_tr(rd + bt_btr_off(k + 4, n));
-      bfr[fn] = u32x4{lo.x, lo.y, hi.x, hi.y};
-    }
-  } else {
-#pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
-      bfr[fn] = *(const u32x4*)(rd + lds_chunk_offset(kBtBM + bt_bcol<G>(wn, fn) + (lane & 31), ch));
-  }
+  for (int fn = 0; fn < 4; ++fn)
+    bfr[fn] = bt_btr(G) ? bt_frag_tr(rd, kBtBM * kBtRB, kg, bt_bcol<G>(wn, fn), lane)
+                        : *(const u32x4*)(rd + lds_chunk_offset(kBtBM + bt_bcol<G>(wn, fn) + (lane & 31), ch));
 }
 
 // One k-step out of ring slot `rd`.  The next k-step's direct-to-LDS loads
@@ -353,12 +371,12 @@ __device__ __forceinline__ void bt_mma(const uint8_t* __restrict__ rd, int wm, i
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn)
-        // DX: weights as the 32-row operand, so a lane holds four consecutive
-        // output columns of one slot row (8-byte bf16 stores)
-        acc[fm][fn] = G == BT_DX ? bt_mfma(bfr[kg & 1][fn], af[kg & 1][fm], acc[fm][fn])
+        // AC, DX: weights as the 32-row operand, so a lane holds four
+        // consecutive output columns of one slot row (8-byte bf16 stores)
+        acc[fm][fn] = bt_swap(G) ? bt_mfma(bfr[kg & 1][fn], af[kg & 1][fm], acc[fm][fn])
                                  : bt_mfma(af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
   }
-  constexpr int NR = bt_btr(G) ? 2 + 8 : 2 + 4;  // LDS reads per k-group
+  constexpr int NR = (bt_atr(G) ? 4 : 2) + (bt_btr(G) ? 8 : 4);  // LDS reads per k-group
   __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
   for (int kg = 0; kg < KG; ++kg) {
@@ -377,22 +395,6 @@ __device__ __forceinline__ void bt_mma(const uint8_t* __restrict__ rd, int wm, i
 
 __device__ __forceinline__ float bt_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.f + __expf(-x));
-}
-
-// Column-major store of a staged [128 columns][256 rows] bfloat16 tile: LDS
-// row i (16-byte chunk c at c ^ (i & 31)) goes to out row (row0 + i), columns
-// col0 + 8c .., for rows i < nrows and chunks c < nchunks.
-__device__ __forceinline__ void bt_store_t(const uint8_t* __restrict__ st, uint16_t* out,
-                                           long long ld, long long row0, long long col0,
-                                           int nrows, int nchunks) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int q = threadIdx.x + k * kBtThreads, i = q >> 5, c = q & 31;
-    if (i < nrows && c < nchunks) {
-      const u32x4 v = *(const u32x4*)(st + i * 512 + ((c ^ (i & 31)) << 4));
-      *(u32x4*)(out + (row0 + i) * ld + col0 + c * 8) = v;
-    }
-  }
 }
 
 struct BtTile {
@@ -425,46 +427,71 @@ __device__ __forceinline__ BtTile bt_tile_of(const BwdArgs& a, const int* s_tab,
 
 // This lane's direct-to-LDS rows of tile t (wavefronts 0-3 the A rows, 4-7 the B
 // rows): a wavefront-uniform base at k = 0 and 32-bit lane offsets.
-template <int G>
-__device__ __forceinline__ const uint8_t* bt_prepare(const BwdArgs& a, const BtTile& t, int wave,
-                                                     int lane, uint32_t (&off)[kBtNI],
-                                                     uint32_t& step) {
-  step = kBtRB;
+// Loading state of one wavefront for a tile: its operand's base at the
+// tile's first k-step, bytes per k-step, and for a slot-major operand the
+// contraction rows that exist and the row pitch in bytes (to bound the range).
+struct BtLoad {
   const uint8_t* base;
-  if (wave < 4) {  // A rows
+  uint32_t step;
+  int rows;      // -1: no bound
+  int pitch_b;
+};
+
+// Range (bytes) the loads of k-step s may touch: rows past the operand's
+// last one read zeros.
+__device__ __forceinline__ int bt_nrec(const BtLoad& l, int s) {
+  if (l.rows < 0) return 0x7fffffff;
+  return min(max(l.rows - 64 * s, 0), 64) * l.pitch_b;
+}
+
+// This lane's direct-to-LDS rows of tile t (wavefronts 0-3 the A operand,
+// 4-7 the B operand): 32-bit lane offsets from the wavefront's base.
+template <int G>
+__device__ __forceinline__ BtLoad bt_prepare(const BwdArgs& a, const BtTile& t, int wave, int lane,
+                                             uint32_t (&off)[kBtNI]) {
+  BtLoad l;
+  l.step = kBtRB;
+  l.rows = -1;
+  l.pitch_b = 0;
+  const bool is_a = wave < 4;
+  if (is_a ? bt_atr(G) : bt_btr(G)) {
+    // stored layout: instruction i of the wavefront moves rows 2(8w + i) and
+    // 2(8w + i) + 1 of the k-step (w = wave % 4); lane L the chunk at position L % 32
+    int pitch, width, rows;
+    const uint16_t* src = bt_tr_src<G>(a, t.v, t.g, pitch, width, rows);
+    const int c0 = is_a ? t.m0 : t.n0;
+    l.base = uni((const uint8_t*)src);
+    l.step = uni(64 * pitch * 2);
+    l.rows = uni(rows);
+    l.pitch_b = uni(pitch * 2);
+#pragma unroll
+    for (int i = 0; i < kBtNI; ++i) {
+      const int k = 2 * ((wave & 3) * kBtNI + i) + (lane >> 5);
+      const int c = (lane & 31) ^ ((k & 7) << 1);
+      // columns past the last one (a partial tile) reread the last chunk
+      const int col = min(c0 + 8 * c, width - 8);
+      off[i] = (uint32_t)(((size_t)k * pitch + col) * 2);
+    }
+  } else if (is_a) {
     constexpr bool gathered = G == BT_DP || G == BT_AC;
-    base = uni(gathered ? (const uint8_t*)(G == BT_DP ? a.dh : a.u)
-                        : bt_a_row<G>(a, t.v, t.g, min(t.m0, t.g.M - 1)));
+    l.base = uni(gathered ? (const uint8_t*)(G == BT_DP ? a.dh : a.u)
+                          : bt_a_row<G>(a, t.v, t.g, min(t.m0, t.g.M - 1)));
 #pragma unroll
     for (int i = 0; i < kBtNI; ++i) {
       const int r = (wave * kBtNI + i) * 8 + (lane >> 3);
       const uint8_t* rp = bt_a_row<G>(a, t.v, t.g, min(t.m0 + r, t.g.M - 1));
-      off[i] = (uint32_t)(rp - base) + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+      off[i] = (uint32_t)(rp - l.base) + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
     }
-  } else if constexpr (bt_btr(G)) {
-    // stored-layout B: instruction i of B wavefront w moves rows 2(8w + i) and
-    // 2(8w + i) + 1 of the k-step; lane L the chunk at position L % 32
-    int pitch, width;
-    base = uni((const uint8_t*)bt_btr_src<G>(a, t.v, pitch, width));
-    step = uni((int)(64 * pitch * 2));
-#pragma unroll
-    for (int i = 0; i < kBtNI; ++i) {
-      const int k = 2 * ((wave - 4) * kBtNI + i) + (lane >> 5);
-      const int c = (lane & 31) ^ ((k & 7) << 1);
-      // columns past the last one (a partial n-tile) reread the last chunk
-      const int col = min(t.n0 + 8 * c, width - 8);
-      off[i] = (uint32_t)(((size_t)k * pitch + col) * 2);
-    }
-  } else {  // B rows, contiguous along the contraction
-    base = uni(bt_b_row<G>(a, t.v, t.n0, 0));
+  } else {
+    l.base = uni(bt_b_row<G>(a, t.v, t.n0, 0));
 #pragma unroll
     for (int i = 0; i < kBtNI; ++i) {
       const int r = ((wave - 4) * kBtNI + i) * 8 + (lane >> 3);
       const uint8_t* rp = bt_b_row<G>(a, t.v, t.n0, r);
-      off[i] = (uint32_t)(rp - base) + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+      off[i] = (uint32_t)(rp - l.base) + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
     }
   }
-  return base;
+  return l;
 }
 
 // AC: the gate of every tile row (rows past the expert's last slot: 0).
@@ -555,120 +582,108 @@ __device__ __forceinline__ void bt_epilogue(const BwdArgs& a, const BtTile& t, i
     return;
   }
 
-  // ---- AC epilogue: the SwiGLU backward of the tile
-  // dP of the tile's rows and columns, p, da, dc; dAC goes out slot-major from
-  // registers; da and dc are staged column-major ([column][row] bfloat16, 512
-  // bytes per column, chunk c at c ^ (column & 31)) in the two ring slots.
+  // ---- AC epilogue: the SwiGLU backward of the tile.  Swapped operands:
+  // acc[fm][fn][4q + e] is slot row wm*64 + fm*32 + lane%32 and column
+  // bt_bcol(wn, fn) + 8q + 4(lane/32) + e (gate fn < 2, up fn + 2, same
+  // columns).  da and dc are staged row-major in the two ring slots ([256
+  // rows][128 columns] bfloat16, chunk c of row r at c ^ (r & 15)), then g p
+  // in the first, and go out as whole 16-byte row chunks.
   const int j = v - a.N;
-  // the tile's dP rows (routed: slot order; shared: token t, expert j)
   const float* dp_base = g.routed ? a.dP + (size_t)g.base * a.I : a.dPs + (size_t)j * a.I;
   const size_t dp_pitch = g.routed ? (size_t)a.I : (size_t)a.K_s * a.I;
+  float dsr[2];
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm) {
+    const int row = wm * 64 + fm * 32 + lc, m = m0 + row;
+    const float gv = s_gate[row];
+    // the row's 32 dP values (eight 16-byte loads) in flight at once
+    f32x4 dpv[2][4];
+#pragma unroll
+    for (int fp = 0; fp < 2; ++fp)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = n0 + bt_bcol<BT_AC>(wn, fp) + 8 * q + 4 * lh;
+        dpv[fp][q] = (m < g.M && i < a.I) ? *(const f32x4*)(dp_base + (size_t)m * dp_pitch + i)
+                                          : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    dsr[fm] = 0.f;
+#pragma unroll
+    for (int fp = 0; fp < 2; ++fp)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float da[4], dc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float dp = dpv[fp][q][e];
+          const float av = acc[fm][fp][4 * q + e], cv = acc[fm][fp + 2][4 * q + e];
+          const float sg = bt_sigmoid(av), sl = av * sg;
+          const float dpg = gv * dp;
+          da[e] = dpg * cv * sg * (1.f + av * (1.f - sg));
+          dc[e] = dpg * sl;
+          dsr[fm] += dp * (sl * cv);
+        }
+        const int col = bt_bcol<BT_AC>(wn, fp) + 8 * q + 4 * lh;  // 0 .. 127
+        const int at = row * 256 + ((((col >> 3) ^ (row & 15))) << 4) + (col & 7) * 2;
+        *(uint2*)(lds0 + at) = uint2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+        *(uint2*)(lds1 + at) = uint2{pack_bf16x2(dc[0], dc[1]), pack_bf16x2(dc[2], dc[3])};
+      }
+    // this wavefront's 64 columns: the two lane halves, then the two column halves
+    const float x = dsr[fm] + __shfl_xor(dsr[fm], 32);
+    if (lh == 0) s_ds[wn][row] = x;
+  }
+  lds_sync();
+  // slot-major copies: thread t moves chunk t % 16 of rows t / 16 + 32k
+  const int ncols = min(kBtBNB / 2, a.I - n0);
   uint16_t* dac_base = g.routed ? (uint16_t*)a.dAC + (size_t)g.base * 2 * a.I
                                 : (uint16_t*)a.dACs + (size_t)j * 2 * a.I;
   const size_t dac_pitch = g.routed ? 2 * (size_t)a.I : (size_t)a.K_s * 2 * a.I;
-  float dsr[2][16];
+  uint16_t* gp_base = g.routed ? (uint16_t*)a.P + (size_t)g.base * a.I : (uint16_t*)a.Ps + (size_t)j * a.I;
+  const size_t gp_pitch = g.routed ? (size_t)a.I : (size_t)a.K_s * a.I;
+  const int cc = tid & 15;
+  const bool col_ok = cc * 8 < ncols;
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm) {
-    // all 32 dP values of this row fragment in flight at once
-    float dpv[2][16];
-#pragma unroll
-    for (int fp = 0; fp < 2; ++fp) {
-      const int i = n0 + bt_bcol<BT_AC>(wn, fp) + lc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        dpv[fp][r] = (m < g.M && i < a.I) ? dp_base[(size_t)m * dp_pitch + i] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dsr[fm][r] = 0.f;
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int row0 = wm * 64 + fm * 32 + 8 * r4 + 4 * lh;  // tile rows row0 .. row0 + 3
-#pragma unroll
-      for (int fp = 0; fp < 2; ++fp) {
-        const int col = bt_bcol<BT_AC>(wn, fp) + lc;  // 0 .. 127
-        const int i = n0 + col;
-        float da[4], dc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = row0 + q;
-          const float dp = dpv[fp][4 * r4 + q];
-          const float av = acc[fm][fp][4 * r4 + q], cv = acc[fm][fp + 2][4 * r4 + q];
-          const float sg = bt_sigmoid(av), sl = av * sg;
-          const float p = sl * cv;
-          const float dpg = s_gate[t] * dp;
-          da[q] = dpg * cv * sg * (1.f + av * (1.f - sg));
-          dc[q] = dpg * sl;
-          dsr[fm][4 * r4 + q] += dp * p;
-        }
-        if (i < a.I) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int m = m0 + row0 + q;
-            if (m < g.M) {
-              uint16_t* dacr = dac_base + (size_t)m * dac_pitch;
-              dacr[i] = f32_to_bf16(da[q]);
-              dacr[a.I + i] = f32_to_bf16(dc[q]);
-            }
-          }
-        }
-        const int sw = ((row0 >> 3) ^ (col & 31)) << 4;
-        uint2 wa, wc;
-        wa.x = pack_bf16x2(da[0], da[1]);
-        wa.y = pack_bf16x2(da[2], da[3]);
-        wc.x = pack_bf16x2(dc[0], dc[1]);
-        wc.y = pack_bf16x2(dc[2], dc[3]);
-        *(uint2*)(lds0 + col * 512 + sw + (row0 & 7) * 2) = wa;
-        *(uint2*)(lds1 + col * 512 + sw + (row0 & 7) * 2) = wc;
-      }
+  for (int k = 0; k < 8; ++k) {
+    const int row = (tid >> 4) + 32 * k, m = m0 + row;
+    const int at = row * 256 + ((cc ^ (row & 15)) << 4);
+    const u32x4 va = *(const u32x4*)(lds0 + at), vc = *(const u32x4*)(lds1 + at);
+    if (m < g.M && col_ok) {
+      uint16_t* r = dac_base + (size_t)m * dac_pitch + n0 + cc * 8;
+      *(u32x4*)r = va;
+      *(u32x4*)(r + a.I) = vc;
     }
   }
-  // partial gate gradients: sum over this wavefront's 64 columns, then the two
-  // column halves of the tile
-#pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = dsr[fm][r];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
-      if (lc == 0) s_ds[wn][wm * 64 + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = x;
-    }
-  lds_sync();
-  const long long cp = bt_colp(a, v) + m0;
-  const int ncols = min(kBtBNB / 2, a.I - n0);
-  const int nch = (min(kBtBM, bt_pad64(g.M) - m0)) >> 3;  // 8-row chunks incl. zero padding
-  bt_store_t(lds0, (uint16_t*)a.dACT, a.ldp, n0, cp, ncols, nch);
-  bt_store_t(lds1, (uint16_t*)a.dACT, a.ldp, (long long)a.I + n0, cp, ncols, nch);
   if (g.routed && tid < kBtBM && m0 + tid < g.M) {
     const int NT = (a.I + kBtBNB / 2 - 1) / (kBtBNB / 2);
     a.dsp[(size_t)(g.base + m0 + tid) * NT + n0 / (kBtBNB / 2)] = s_ds[0][tid] + s_ds[1][tid];
   }
   lds_sync();
-  // (g p)^T, recomputed from the accumulators
+  // g p, recomputed from the accumulators
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
+  for (int fm = 0; fm < 2; ++fm) {
+    const int row = wm * 64 + fm * 32 + lc;
+    const float gv = s_gate[row];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int row0 = wm * 64 + fm * 32 + 8 * r4 + 4 * lh;
+    for (int fp = 0; fp < 2; ++fp)
 #pragma unroll
-      for (int fp = 0; fp < 2; ++fp) {
-        const int col = bt_bcol<BT_AC>(wn, fp) + lc;
+      for (int q = 0; q < 4; ++q) {
         float gp[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float av = acc[fm][fp][4 * r4 + q], cv = acc[fm][fp + 2][4 * r4 + q];
-          gp[q] = s_gate[row0 + q] * (av * bt_sigmoid(av) * cv);
+        for (int e = 0; e < 4; ++e) {
+          const float av = acc[fm][fp][4 * q + e], cv = acc[fm][fp + 2][4 * q + e];
+          gp[e] = gv * (av * bt_sigmoid(av) * cv);
         }
-        uint2 w;
-        w.x = pack_bf16x2(gp[0], gp[1]);
-        w.y = pack_bf16x2(gp[2], gp[3]);
-        *(uint2*)(lds0 + col * 512 + (((row0 >> 3) ^ (col & 31)) << 4) + (row0 & 7) * 2) = w;
+        const int col = bt_bcol<BT_AC>(wn, fp) + 8 * q + 4 * lh;
+        const int at = row * 256 + ((((col >> 3) ^ (row & 15))) << 4) + (col & 7) * 2;
+        *(uint2*)(lds0 + at) = uint2{pack_bf16x2(gp[0], gp[1]), pack_bf16x2(gp[2], gp[3])};
       }
-    }
+  }
   lds_sync();
-  bt_store_t(lds0, (uint16_t*)a.gPT, a.ldp, n0, cp, ncols, nch);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = (tid >> 4) + 32 * k, m = m0 + row;
+    const u32x4 vg = *(const u32x4*)(lds0 + row * 256 + ((cc ^ (row & 15)) << 4));
+    if (m < g.M && col_ok) *(u32x4*)(gp_base + (size_t)m * gp_pitch + n0 + cc * 8) = vg;
+  }
 }
 
 // Grouped k-major GEMM C = A B^T for product G (bfloat16 operands, float32
@@ -731,14 +746,15 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
   const int claim_base = start + stride;
 
   BtTile cur = bt_tile_of<G>(a, s_tab, V, L);
-  uint32_t off[kBtNI], step;
-  const uint8_t* base = bt_prepare<G>(a, cur, wave, lane, off, step);
+  uint32_t off[kBtNI];
+  BtLoad ld = bt_prepare<G>(a, cur, wave, lane, off);
   if (G == BT_AC) bt_fill_gate(a, cur, s_gate);
   int ph = 0;  // ring slot of the current tile's k-step 0
   if (cur.steps > 0) {
     uint8_t* w = lds0 + wave * kBtNI * 1024;
+    const int nrec = bt_nrec(ld, 0);
 #pragma unroll
-    for (int i = 0; i < kBtNI; ++i) dma16(base, off[i], w + i * 1024);
+    for (int i = 0; i < kBtNI; ++i) dma16(ld.base, off[i], w + i * 1024, nrec);
   }
   for (int it = 0;; ++it) {
     if (kPersist && tid == 0) s_claim[it & 1] = claim_base + atomicAdd(ctr, 1);
@@ -759,11 +775,12 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
       Ln = uni(s_claim[it & 1]);
       if (G != BT_AC && Ln < end) {
         nxt = bt_tile_of<G>(a, s_tab, V, Ln);
-        base = bt_prepare<G>(a, nxt, wave, lane, off, step);
+        ld = bt_prepare<G>(a, nxt, wave, lane, off);
         pre = true;
         uint8_t* w = ((ph & 1) ? lds1 : lds0) + wave * kBtNI * 1024;
+        const int nrec = nxt.steps > 0 ? bt_nrec(ld, 0) : 0;
 #pragma unroll
-        for (int i = 0; i < kBtNI; ++i) dma16(base, off[i], w + i * 1024, nxt.steps > 0 ? 0x7fffffff : 0);
+        for (int i = 0; i < kBtNI; ++i) dma16(ld.base, off[i], w + i * 1024, nrec);
       }
     }
     for (int s = 0; s < cur.steps; ++s) {
@@ -771,21 +788,21 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
       const int q = (ph + s) & 1;
       const uint8_t* rd = q ? lds1 : lds0;
       uint8_t* wr = (q ? lds0 : lds1) + wave * kBtNI * 1024;
-      const uint8_t* db = base + (size_t)(s + 1) * step;
-      int nrec = 0x7fffffff;
+      const uint8_t* db = ld.base + (size_t)(s + 1) * ld.step;
+      int nrec = bt_nrec(ld, s + 1);
       if (s + 1 == cur.steps) {
         Ln = kPersist ? uni(s_claim[it & 1]) : end;
         nrec = 0;
-        db = base;
+        db = ld.base;
         if (G != BT_AC && Ln < end) {
           nxt = bt_tile_of<G>(a, s_tab, V, Ln);
-          base = bt_prepare<G>(a, nxt, wave, lane, off, step);
-          db = base;
+          ld = bt_prepare<G>(a, nxt, wave, lane, off);
+          db = ld.base;
           pre = true;
-          if (nxt.steps > 0) nrec = 0x7fffffff;
+          if (nxt.steps > 0) nrec = bt_nrec(ld, 0);
         }
       }
-      bt_mma<G>(rd, wm, wn, lane, acc, uni(db), off, wr, nrec);
+      bt_mma<G>(rd, wm, wn, lane, acc, uni(db), off, wr, uni(nrec));
     }
     if (G == BT_AC) pipe_sync();  // the ring is free for the staged epilogue
     bt_epilogue<G>(a, cur, wm, wn, lane, acc, lds0, lds1, s_gate, s_ds);

@@ -425,8 +425,8 @@ struct BwdLayout {
       tab, total;
   // pipelined bfloat16 path
   bool pipe;
-  size_t XT, dhT, dACT, gPT, dsp, tabs;
-  long long ldx, ldp;
+  size_t XT, dhT, dsp, tabs;
+  long long ldx;
 };
 
 int pad8(int n) { return (n + 7) & ~7; }
@@ -465,8 +465,8 @@ BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype)
   L.dPs = take((size_t)T * K_s * I * 4);
   L.dAC = take(TK * 2 * I * es);
   L.dACs = take((size_t)T * K_s * 2 * I * es);
-  L.P = take(gen * TK * I * es);
-  L.Ps = take(gen * (size_t)T * K_s * I * es);
+  L.P = take(TK * I * es);
+  L.Ps = take((size_t)T * K_s * I * es);
   L.dY = take(gen * TK * d * es);
   L.dX = take(TK * d * 4);
   L.dXs = take((size_t)K_s * T * d * 4);
@@ -479,11 +479,8 @@ BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype)
   if (L.pipe) {
     const long long R = moe::bt_routed_cols(T, K, N), Tp = moe::bt_pad64(T);
     L.ldx = R + Tp;
-    L.ldp = R + (long long)K_s * Tp;
     L.XT = take((size_t)d * L.ldx * 2);
     L.dhT = take((size_t)d * L.ldx * 2);
-    L.dACT = take((size_t)2 * I * L.ldp * 2);
-    L.gPT = take((size_t)I * L.ldp * 2);
     L.dsp = take(TK * ((I + 127) / 128) * 4);
     L.tabs = take((size_t)(moe::bt_tables_ints(N, K_s) + N + 1) * 4);
   }
@@ -587,12 +584,9 @@ moe_status_t moe_layer_backward(const void* u, const void* E_gate, const void* W
     tabs = (int32_t*)(ws + L.tabs);
     a.XT = ws + L.XT;
     a.dhT = ws + L.dhT;
-    a.dACT = ws + L.dACT;
-    a.gPT = ws + L.gPT;
     a.dsp = (float*)(ws + L.dsp);
     a.pcol = tabs + moe::bt_tables_ints(N, K_s);
     a.ldx = L.ldx;
-    a.ldp = L.ldp;
     a.Tp = moe::bt_pad64(T);
   }
   if ((e = moe::launch_backward(dtype, a, gate, scores, idx, (float*)(ws + L.ds_pair),

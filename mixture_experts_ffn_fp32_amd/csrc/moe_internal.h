@@ -134,7 +134,7 @@ struct BwdArgs {
   float* dPs;                  // [T][K_s*I]
   void* dAC;                   // [T*K][2I] dtype  [da, dc]
   void* dACs;                  // [T][K_s*2I]
-  void* P;                     // [T*K][I] dtype   p = SiLU(a) c
+  void* P;                     // [T*K][I] dtype   p = SiLU(a) c (bf16 path: g p)
   void* Ps;                    // [T][K_s*I]
   void* dY;                    // [T*K][d] dtype   g * dh rows
   float* dX;                   // [T*K][d]       W_gate^T da + W_up^T dc (routed slots)
@@ -149,11 +149,9 @@ struct BwdArgs {
   const float* gate;           // [T*K] kept gates by pair
   void* XT;                    // [d][ldx]    u^T over the padded slot columns
   void* dhT;                   // [d][ldx]    dh^T over the same columns
-  void* dACT;                  // [2I][ldp]   [da, dc]^T over the padded slot columns
-  void* gPT;                   // [I][ldp]    (g p)^T
   float* dsp;                  // [T*K][ceil(I/128)] partial gate gradients per 128 columns
   int32_t* pcol;               // [N+1] padded first column of each routed expert
-  long long ldx, ldp;          // row pitches (elements) of XT/dhT and dACT/gPT
+  long long ldx;               // row pitch (elements) of XT and dhT
   int Tp;                      // T rounded up to 64: the shared experts' column count
 };
 int backward_de_chunks(int T);
