@@ -42,11 +42,6 @@ constexpr int kBtMaxV = 256 + 16;
 
 __host__ __device__ constexpr int bt_bn(int G) { return G == BT_AC ? kBtBNB / 2 : kBtBNB; }
 
-__device__ __forceinline__ int bt_xcd_swizzle(int b, int G) {
-  const int x = b & 7, q = G >> 3, r = G & 7;
-  return x * q + min(x, r) + (b >> 3);
-}
-
 struct BtGroup {
   int M, Nc, steps, rows, base;
   bool routed;
@@ -686,7 +681,7 @@ __device__ __forceinline__ void bt_epilogue(const BwdArgs& a, const BtTile& t, i
   }
 }
 
-// Grouped k-major GEMM C = A B^T for product G (bfloat16 operands, float32
+// Grouped GEMM C = A B^T for product G (bfloat16 operands, float32
 // accumulation).  Persistent, one block per CU, 256 x bt_bn(G) tiles.
 // Slot-row products: each XCD (blocks are dealt to the XCDs round-robin)
 // owns a contiguous range of tiles (m fastest: the tiles of one weight tile
@@ -713,16 +708,8 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
   __syncthreads();
   const int total = s_tab[V];
   constexpr bool kWgrad = G == BT_DWD || G == BT_DWGC;
-  // AC keeps one tile per block: its staged epilogue needs every register
-  // the loop state would hold
-  constexpr bool kPersist = G != BT_AC;
   int start, end, stride, x;
-  if (!kPersist) {
-    start = 0;
-    end = total;
-    stride = 0;
-    x = 0;
-  } else if (kWgrad) {
+  if (kWgrad) {
     start = 0;
     end = total;
     stride = gridDim.x;
@@ -734,14 +721,8 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
     end = (int)((long long)total * (x + 1) / X);
     stride = ((int)gridDim.x - x + X - 1) / X;
   }
-  int L;
-  if (!kPersist) {
-    if ((int)blockIdx.x >= total) return;
-    L = bt_xcd_swizzle(blockIdx.x, total);
-  } else {
-    L = start + (kWgrad ? (int)blockIdx.x : (int)blockIdx.x / min(8, (int)gridDim.x));
-    if (L >= end) return;
-  }
+  const int L = start + (kWgrad ? (int)blockIdx.x : (int)blockIdx.x / min(8, (int)gridDim.x));
+  if (L >= end) return;
   int32_t* const ctr = counters + x;
   const int claim_base = start + stride;
 
@@ -757,7 +738,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
     for (int i = 0; i < kBtNI; ++i) dma16(ld.base, off[i], w + i * 1024, nrec);
   }
   for (int it = 0;; ++it) {
-    if (kPersist && tid == 0) s_claim[it & 1] = claim_base + atomicAdd(ctr, 1);
+    if (tid == 0) s_claim[it & 1] = claim_base + atomicAdd(ctr, 1);
     f32x16 acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -768,7 +749,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
     int Ln = end;
     BtTile nxt = cur;
     bool pre = false;  // the next tile's first k-step was issued under this tile
-    if (kPersist && cur.steps == 0) {
+    if (cur.steps == 0) {
       // (the wait also lands the zero loads issued into this slot under the
       // previous tile before the slot is loaded again)
       pipe_sync();
@@ -791,7 +772,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
       const uint8_t* db = ld.base + (size_t)(s + 1) * ld.step;
       int nrec = bt_nrec(ld, s + 1);
       if (s + 1 == cur.steps) {
-        Ln = kPersist ? uni(s_claim[it & 1]) : end;
+        Ln = uni(s_claim[it & 1]);
         nrec = 0;
         db = ld.base;
         if (G != BT_AC && Ln < end) {
@@ -807,8 +788,22 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
     if (G == BT_AC) pipe_sync();  // the ring is free for the staged epilogue
     bt_epilogue<G>(a, cur, wm, wn, lane, acc, lds0, lds1, s_gate, s_ds);
     ph += cur.steps;
-    // a persistent product always issued the next tile's first k-step above
-    if (!kPersist || Ln >= end || !pre) break;
+    if (Ln >= end) break;
+    if (!pre) {
+      // AC: its epilogue staged through the ring, so the next tile's first
+      // k-step is loaded only now (the zero loads of the last k-step landed
+      // before the epilogue)
+      __syncthreads();
+      nxt = bt_tile_of<G>(a, s_tab, V, Ln);
+      ld = bt_prepare<G>(a, nxt, wave, lane, off);
+      if (G == BT_AC) bt_fill_gate(a, nxt, s_gate);
+      if (nxt.steps > 0) {
+        uint8_t* w = ((ph & 1) ? lds1 : lds0) + wave * kBtNI * 1024;
+        const int nrec = bt_nrec(ld, 0);
+#pragma unroll
+        for (int i = 0; i < kBtNI; ++i) dma16(ld.base, off[i], w + i * 1024, nrec);
+      }
+    }
     cur = nxt;
   }
   MOE_WAIT_VMCNT(0);  // no direct-to-LDS load outlives the block
@@ -858,7 +853,7 @@ hipError_t bt_launch(const BwdArgs& a, int32_t* tabs, hipStream_t st) {
   const long long ub = bt_grid(G, a);
   if (ub <= 0) return hipSuccess;
   const int V = a.N + a.K_s;
-  const long long grid = G == BT_AC ? ub : std::min<long long>(ub, bt_cu_count());
+  const long long grid = std::min<long long>(ub, bt_cu_count());
   bt_gemm_kernel<G><<<dim3((unsigned)grid), dim3(kBtThreads), 0, st>>>(
       a, tabs + (G - 1) * (V + 1), tabs + BT_NG * (V + 1) + (G - 1) * 8);
   return hipGetLastError();
