@@ -225,6 +225,138 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
   }
 }
 
+// Small batches (decode): one block per token.  Each of the 256 threads takes
+// 16-byte chunks of the token's row and multiplies them with the same chunks
+// of every expert row (E_gate stays in L2 across the blocks); the 64 partial
+// logits of an expert group are reduced across the wavefront by a halving
+// exchange (each lane ends with one expert's sum), then across the four
+// wavefronts in LDS in a fixed order.  Softmax and top-K run on the first
+// wavefront, each lane holding experts lane, lane + 64, ...
+constexpr int kSmallRouterMaxT = 128;
+
+// Element q of a 16-byte chunk as float32.
+__device__ __forceinline__ float chunk_elem(ElemBF16, u32x4 w, int q) {
+  return __uint_as_float((q & 1) ? (w[q >> 1] & 0xffff0000u) : (w[q >> 1] << 16));
+}
+__device__ __forceinline__ float chunk_elem(ElemF32, u32x4 w, int q) { return __uint_as_float(w[q]); }
+
+template <class E>
+__global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* __restrict__ u,
+                                                           const typename E::T* __restrict__ Eg,
+                                                           const float* __restrict__ bias, int T,
+                                                           int d, int N, int K,
+                                                           int32_t* __restrict__ idx,
+                                                           float* __restrict__ gate,
+                                                           float* __restrict__ scores) {
+  using Tp = typename E::T;
+  constexpr int PC = E::kPerChunk;
+  __shared__ float s_red[4][64];
+  __shared__ float s_logit[256];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = d / PC;  // 16-byte chunks per row
+  const Tp* ur = u + (size_t)t * d;
+  for (int eb = 0; eb < N; eb += 64) {
+    float part[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) part[i] = 0.f;
+    for (int c = tid; c < nch; c += 256) {
+      const u32x4 xu = *(const u32x4*)(ur + c * PC);
+      float x[PC];
+#pragma unroll
+      for (int q = 0; q < PC; ++q) x[q] = chunk_elem(E{}, xu, q);
+      // 32 expert chunks in flight per batch
+#pragma unroll
+      for (int ib = 0; ib < 64; ib += 32) {
+        u32x4 w[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int e = min(eb + ib + i, N - 1);  // experts past N: a valid row, never used
+          w[i] = *(const u32x4*)(Eg + (size_t)e * d + c * PC);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          float acc = 0.f;
+#pragma unroll
+          for (int q = 0; q < PC; ++q) acc += x[q] * chunk_elem(E{}, w[i], q);
+          part[ib + i] += acc;
+        }
+      }
+    }
+    // halving exchange: after step s a lane holds 32 >> s partial sums of the
+    // experts whose index agrees with the lane in the bits already folded
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) {
+      const bool upper = (lane & h) != 0;
+#pragma unroll
+      for (int i = 0; i < h; ++i) {
+        // keep expert (upper ? i + h : i) of each pair; send the other
+        const float send = upper ? part[i] : part[i + h];
+        const float recv = __shfl_xor(send, h);
+        part[i] = (upper ? part[i + h] : part[i]) + recv;
+      }
+    }
+    // lane l now holds the wavefront's sum for expert eb + l
+    s_red[wave][lane] = part[0];
+    __syncthreads();
+    if (wave == 0 && eb + lane < N)
+      s_logit[eb + lane] = ((s_red[0][lane] + s_red[1][lane]) + s_red[2][lane]) + s_red[3][lane];
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  float v[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < N ? s_logit[e] + (bias ? bias[e] : 0.f) : -INFINITY;
+    m = fmaxf(m, v[j]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < N ? expf(v[j] - m) : 0.f;
+    sum += v[j];
+  }
+  // butterfly: every lane ends with the same bits
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < N ? v[j] / sum : -2.f;  // scores are >= 0; -2 marks padding
+    if (scores != nullptr && e < N) scores[(size_t)t * N + e] = v[j];
+  }
+  for (int k = 0; k < K; ++k) {
+    float bv = -1.f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)  // ascending expert id within the lane
+      if (v[j] > bv) {
+        bv = v[j];
+        bi = lane + 64 * j;
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j == bi) v[j] = -1.f;  // taken (-1 is below every score)
+    if (lane == 0) {
+      idx[(size_t)t * K + k] = bi;
+      gate[(size_t)t * K + k] = bv;
+    }
+  }
+}
+
 template <class E, int F, int TB>
 hipError_t launch_router_tb(const void* u, const void* Eg, const float* bias, int T, int d, int N,
                             int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
@@ -254,6 +386,13 @@ int router_tb(int T) {
   return v;
 }
 
+// Batches of at most kSmallRouterMaxT tokens take the one-block-per-token
+// kernel unless MOE_ROUTER_SMALL=0.
+bool router_small() {
+  const char* e = getenv("MOE_ROUTER_SMALL");
+  return !(e != nullptr && e[0] == '0');
+}
+
 template <class E, int F>
 hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int T, int d, int N,
                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
@@ -267,6 +406,12 @@ hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int
 template <class E>
 hipError_t launch_router_t(const void* u, const void* Eg, const float* bias, int T, int d, int N,
                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
+  using Tp = typename E::T;
+  if (T <= kSmallRouterMaxT && router_small()) {
+    router_small_kernel<E><<<T, 256, 0, st>>>((const Tp*)u, (const Tp*)Eg, bias, T, d, N, K, idx,
+                                              gate, scores);
+    return hipGetLastError();
+  }
   if (N <= 16) return launch_router_f<E, 1>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
   if (N <= 32) return launch_router_f<E, 2>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
   if (N <= 64) return launch_router_f<E, 4>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);

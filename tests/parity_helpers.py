@@ -147,6 +147,10 @@ SMALL = {
     # shared one) at a reduced size: I0 = 4096, d = 128
     "gran_m1_ks0_bf16": dict(T=300, d=128, N=16, K=2, K_s=0, I=4096, dtype="bf16", seed=1101),
     "gran_m8_ks1_bf16": dict(T=300, d=128, N=127, K=15, K_s=1, I=512, dtype="bf16", seed=1181),
+    # decode-sized batches (the one-block-per-token router): many experts, a ragged
+    # expert count, float32
+    "decode_n256_bf16": dict(T=96, d=256, N=256, K=8, K_s=1, I=128, dtype="bf16", seed=1201),
+    "decode_n200_f32": dict(T=100, d=192, N=200, K=5, K_s=0, I=64, dtype="f32", seed=1202),
 }
 
 

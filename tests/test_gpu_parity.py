@@ -36,6 +36,24 @@ def test_route(small):
     check_routing(idx.cpu().numpy(), gate.cpu().numpy(), s_ref, w.K)
 
 
+@pytest.mark.parametrize("name", ["decode_n256_bf16", "one_token_bf16", "k_equals_n_f32"])
+def test_route_small_batch_kernels_agree(name, monkeypatch):
+    """Batches of at most 128 tokens use the one-block-per-token router; the tiled
+    router (MOE_ROUTER_SMALL=0) must give the same routing wherever the margin is
+    clear, and both must meet the oracle's bar."""
+    up = Uploaded(small_inputs(name))
+    w = up.w
+    say(f"route small-batch kernels {w.name}")
+    idx_s, gate_s, sc_s = mx.route(up.u, up.E, w.K, up.bias, want_scores=True)
+    monkeypatch.setenv("MOE_ROUTER_SMALL", "0")
+    idx_t, gate_t, sc_t = mx.route(up.u, up.E, w.K, up.bias, want_scores=True)
+    torch.cuda.synchronize()
+    s_ref = oracle.affinity_scores(up.inp.u_f32(), up.inp.E_gate_f32(), up.inp.gate_bias())
+    for idx, gate, sc in ((idx_s, gate_s, sc_s), (idx_t, gate_t, sc_t)):
+        assert np.all(np.abs(sc.cpu().numpy() - s_ref) <= 1e-5 * s_ref + 1e-9)
+        check_routing(idx.cpu().numpy(), gate.cpu().numpy(), s_ref, w.K)
+
+
 def test_dispatch(small):
     w = small.w
     s_ref = oracle.affinity_scores(small.inp.u_f32(), small.inp.E_gate_f32(), small.inp.gate_bias())
