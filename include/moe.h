@@ -205,7 +205,8 @@ moe_status_t moe_layer_backward(const void* u, const void* E_gate, const void* W
 #define MOE_NUM_STAGES 7
 /* stage order: 0 router, 1 tile ranks, 2 dispatch scan, 3 scatter,
  *              4 expert GEMM1 (gate/up + SwiGLU), 5 expert GEMM2 (down x gate),
- *              6 combine.  The tile-table kernel is counted in stage 4. */
+ *              6 combine.  The tile-table kernel is counted in stage 4; a batch
+ *              of at most 64 tokens runs the whole dispatch as stage 1. */
 moe_status_t moe_timing_enable(int on);
 moe_status_t moe_timing_read(double* ms_per_stage, int* launches_per_stage);
 

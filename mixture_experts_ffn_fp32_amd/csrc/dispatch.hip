@@ -12,6 +12,7 @@
 //  2. dispatch_scan: one block turns tile counts into per-expert totals,
 //     offsets (exclusive scan over experts) and per-(tile, expert) bases.
 //  3. scatter: sorted_pair[base + rank] = p.
+// A batch of at most 64 tokens (decode) does all three in one launch.
 #include "moe_internal.h"
 
 namespace moe {
@@ -127,7 +128,57 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   sorted_pair[tile_base[(size_t)(t / kRankTile) * N + e] + rank[p]] = (int32_t)p;
 }
 
+// A batch of at most 64 tokens in one launch (one wavefront, lane = token):
+// the lane masks of step 1 for the single tile, then the expert counts, their
+// exclusive scan and the scatter -- the same ranks and order as steps 1-3.
+__global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __restrict__ idx,
+                                                            int T, int N, int K,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_pair) {
+  __shared__ unsigned long long mask[256];
+  __shared__ int s_off[257];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < N; e += 64) mask[e] = 0ull;
+  __syncthreads();
+  const unsigned long long bit = 1ull << lane;
+  if (lane < T)
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[(size_t)lane * K + k];
+      if ((unsigned)e < (unsigned)N) atomicOr(&mask[e], bit);
+    }
+  __syncthreads();
+  int carry = 0;
+  for (int b = 0; b < N; b += 64) {
+    const int e = b + lane;
+    const int c = e < N ? __popcll(mask[e]) : 0;
+    const int inc = wave_inclusive_scan(c);
+    if (e < N) {
+      counts[e] = c;
+      s_off[e] = carry + inc - c;
+      offsets[e] = carry + inc - c;
+    }
+    carry += __shfl(inc, 63);
+  }
+  if (lane == 0) offsets[N] = carry;
+  __syncthreads();
+  if (lane < T) {
+    const unsigned long long below = bit - 1ull;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[(size_t)lane * K + k];
+      if ((unsigned)e < (unsigned)N)
+        sorted_pair[s_off[e] + __popcll(mask[e] & below)] = lane * K + k;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dispatch_small(const int32_t* idx, int T, int N, int K, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pair, hipStream_t stream) {
+  dispatch_small_kernel<<<1, 64, 0, stream>>>(idx, T, N, K, counts, offsets, sorted_pair);
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_rank(const int32_t* idx, int T, int N, int K, int32_t* tile_counts,
                             int32_t* rank, hipStream_t stream) {

@@ -171,6 +171,13 @@ moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* coun
                           int32_t* offsets, int32_t* sorted_pair, int32_t* rank,
                           int32_t* tile_counts, int32_t* tile_base, hipStream_t st) {
   hipError_t e;
+  if (T <= moe::kRankTile) {  // one tile: ranks, scan and scatter in one launch
+    StageScope sc(1, st);
+    if ((e = moe::launch_dispatch_small(idx, T, N, K, counts, offsets, sorted_pair, st)) !=
+        hipSuccess)
+      return hip_fail(e, "dispatch launch");
+    return MOE_OK;
+  }
   {
     StageScope sc(1, st);
     if ((e = moe::launch_tile_rank(idx, T, N, K, tile_counts, rank, st)) != hipSuccess)

@@ -80,6 +80,8 @@ hipError_t launch_tile_rank(const int32_t* idx, int T, int N, int K, int32_t* ti
                             int32_t* rank, hipStream_t stream);
 hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, int32_t* counts,
                                 int32_t* offsets, int32_t* tile_base, hipStream_t stream);
+hipError_t launch_dispatch_small(const int32_t* idx, int T, int N, int K, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pair, hipStream_t stream);
 hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_base,
                           int T, int N, int K, int32_t* sorted_pair, hipStream_t stream);
 
