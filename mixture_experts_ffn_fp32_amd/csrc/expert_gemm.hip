@@ -826,6 +826,18 @@ __device__ __forceinline__ int str_steps(const ExpertArgs& a, const Tile& ti) {
   return (MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I)) / 64;
 }
 
+// Tiles are dealt to the blocks by stride (block b takes b, b + G, ...), so
+// the first total % G blocks take one more tile than the rest.  GEMM2's shared
+// tiles (the last of the table) contract over K_s * I and cost K_s routed
+// tiles: they are moved to the positions just past those blocks, so a block
+// that takes one does not also take the extra tile.
+__device__ __forceinline__ int str_perm(int p, int total, int G, int E) {
+  const int r = total % G;
+  if (E == 0 || r + E > G || p < r) return p;
+  if (p < r + E) return total - E + (p - r);
+  return p - E;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void expert_gemm_stream_kernel(ExpertArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStrS * kStrSlot];
@@ -837,16 +849,17 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_stream_kernel(ExpertArgs a
   const int total = s_tab[V] * nt;
   const int G = gridDim.x;
   if ((int)blockIdx.x >= total) return;  // whole block: no barrier is left behind
+  const int E = (MODE == 2 && a.K_s > 1) ? (s_tab[V] - s_tab[V - 1]) * nt : 0;
   // the block's k-steps, over its tiles blockIdx.x, + G, ...
   int nsteps_all = 0;
   for (int L = blockIdx.x; L < total; L += G)
-    nsteps_all += str_steps<MODE>(a, tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+    nsteps_all += str_steps<MODE>(a, tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, str_perm(L, total, G, E)));
 
   if (wave >= 2) {
     // ---- loading wavefronts: rows (wave - 2) * 80 .. + 79 of each slot
     const int w2 = wave - 2;
     int L = blockIdx.x, s = 0;
-    Tile ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+    Tile ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, str_perm(L, total, G, E)));
     int ns = str_steps<MODE>(a, ti);
     uint32_t off[kStrNI];
     const uint8_t* a_base = nullptr;
@@ -882,7 +895,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_stream_kernel(ExpertArgs a
       } else if (L + G < total) {
         L += G;
         s = 0;
-        ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+        ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, str_perm(L, total, G, E)));
         ns = str_steps<MODE>(a, ti);
         prepare();
       }
@@ -905,7 +918,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_stream_kernel(ExpertArgs a
   // ---- computing wavefronts: B rows wave * 64 .. + 63 (two 32-row fragments)
   const int lc = lane & 31, lh = lane >> 5;
   int L = blockIdx.x, s = 0, slot = 0;
-  Tile ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+  Tile ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, str_perm(L, total, G, E)));
   int ns = str_steps<MODE>(a, ti);
   f32x16 acc[2];
 #pragma unroll
@@ -978,7 +991,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_stream_kernel(ExpertArgs a
     s = 0;
     L += G;
     if (L < total) {
-      ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, L));
+      ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, str_perm(L, total, G, E)));
       ns = str_steps<MODE>(a, ti);
     }
   }
