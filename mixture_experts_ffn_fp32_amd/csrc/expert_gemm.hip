@@ -669,30 +669,52 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   const bool is_a = wave * NINST < kPipeBM / 8;
 
   // Persistent: the blocks of XCD x (blockIdx % 8, workgroups are dealt
-  // round-robin over the XCDs) walk that XCD's contiguous range of tiles, so
-  // concurrent tiles share an expert's weights and tokens in the XCD's L2.
-  // The ranges split the work, not the tile count: a GEMM2 tile of the shared
-  // experts contracts over K_s * I and costs K_s routed tiles.  Inside a
-  // range, each block takes one tile by its index and then claims the next
-  // unprocessed one from the range's counter, so blocks that drew cheap
-  // tiles (an expert's last, partly filled m-tile) take more of them.
+  // round-robin over the XCDs) walk that XCD's contiguous share of the tiles,
+  // so concurrent tiles share an expert's weights and tokens in the XCD's L2.
+  // A GEMM2 tile of the shared experts contracts over K_s * I and costs K_s
+  // routed tiles: every XCD then takes an equal share of those first (the
+  // long tiles start early) and an equal share of the routed tiles after
+  // them.  Each block takes one tile by its index in its XCD's share, then
+  // claims the next one from the share's counter; when its XCD has none
+  // left it claims from the other XCDs' (the XCDs run at different clocks).
   const int V = load_tile_table<MODE>(a, s_tab);
   const int nt = ((MODE == 1 ? a.I : a.d) + BNO - 1) / BNO;
   const int total = s_tab[V] * nt;
   const int Lr = MODE == 2 ? s_tab[a.N] * nt : total;  // tiles before the shared ones
-  const int w = MODE == 2 ? max(a.K_s, 1) : 1;
-  const long long Wt = Lr + (long long)(total - Lr) * w;
+  const int S = total - Lr;                            // GEMM2's shared tiles
+  const bool split = MODE == 2 && a.K_s > 1 && S > 0;
   const int X = min(8, (int)gridDim.x);
   const int x = blockIdx.x % X, lb = blockIdx.x / X;
-  const int nbx = ((int)gridDim.x - x + X - 1) / X;
-  // first tile whose cumulative cost reaches c
-  auto first_at = [&](long long c) -> int {
-    return c <= Lr ? (int)c : Lr + (int)((c - Lr + w - 1) / w);
+  auto part = [&](int n, int y) { return (int)((long long)n * y / X); };
+  auto n_of = [&](int y) -> int {  // tiles in XCD y's share
+    return split ? (part(S, y + 1) - part(S, y)) + (part(Lr, y + 1) - part(Lr, y))
+                 : part(total, y + 1) - part(total, y);
   };
-  const int start = first_at(Wt * x / X), end = first_at(Wt * (x + 1) / X);
-  int L = start + lb;
-  if (L >= end) return;
-  int* const claims = a.counters + (MODE - 1) * 8 + x;
+  auto map = [&](int y, int p) -> int {  // position p of XCD y's share -> tile
+    if (split) {
+      const int ns = part(S, y + 1) - part(S, y);
+      return p < ns ? Lr + part(S, y) + p : part(Lr, y) + (p - ns);
+    }
+    return part(total, y) + p;
+  };
+  int* const ctr = a.counters + (MODE - 1) * 8;
+  // the next tile: from the own XCD's counter first, then the others' (-1: none)
+  auto claim_next = [&]() -> int {
+    for (int k = 0; k < X; ++k) {
+      const int y = x + k < X ? x + k : x + k - X;
+      const int p = ((int)gridDim.x - y + X - 1) / X + atomicAdd(ctr + y, 1);
+      if (p < n_of(y)) return map(y, p);
+    }
+    return -1;
+  };
+  int L = lb < n_of(x) ? map(x, lb) : -1;
+  if (L < 0) {
+    if (tid == 0) s_claim = claim_next();
+    __syncthreads();
+    L = uni(s_claim);
+    __syncthreads();  // read by all before the first tile's claim rewrites it
+    if (L < 0) return;
+  }
 
   Tile ti = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, L));
   PipeLoads<NINST> ld;
@@ -715,9 +737,9 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
     // of the first k-step: the wait for the counter's reply then coincides
     // with the wait for that k-step's loads (with only two k-steps it is
     // claimed at once).
-    int claim = 0;
-    if (nsteps == 2 && tid == 0) claim = atomicAdd(claims, 1);
-    int Ln = end;
+    int claim = -1;
+    if (nsteps == 2 && tid == 0) claim = claim_next();
+    int Ln = -1;
     bool has_next = false;
     // destination row and gate of tile row `tid`, kept in registers until the epilogue
     int my_dst = -1;
@@ -734,18 +756,18 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
 
     Tile tn = ti;
     for (int s = 0; s < nsteps; s += 2) {
-      if (s + 2 >= nsteps && tid == 0) s_claim = start + nbx + claim;
+      if (s + 2 >= nsteps && tid == 0) s_claim = claim;
       // even k-step: slot 0 holds k-step s; k-step s + 1 goes to slot 1
       pipe_sync();
       pipe_mma<E, MODE, FM>(lds0, wm, wn, lane, acc, active,
                             pipe_dma_base<E, MODE>(a, ti, ld, s + 1 < nreal ? s + 1 : 0, is_a),
                             ld.off, lds1 + wave * NINST * 1024, s + 1 < nreal ? 0x7fffffff : 0);
-      if (s == 0 && nsteps > 2 && tid == 0) claim = atomicAdd(claims, 1);
+      if (s == 0 && nsteps > 2 && tid == 0) claim = claim_next();
       // odd k-step: slot 1 holds k-step s + 1; slot 0 gets k-step s + 2, or
       // the next tile's first k-step after the last one
       if (s + 2 >= nsteps) {
         Ln = uni(s_claim);
-        has_next = Ln < end;
+        has_next = Ln >= 0;
       }
       if (s + 2 >= nsteps && has_next) {
         tn = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, Ln));
