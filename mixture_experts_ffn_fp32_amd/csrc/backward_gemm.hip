@@ -723,8 +723,22 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
   }
   const int L = start + (kWgrad ? (int)blockIdx.x : (int)blockIdx.x / min(8, (int)gridDim.x));
   if (L >= end) return;
-  int32_t* const ctr = counters + x;
-  const int claim_base = start + stride;
+  // the next tile (-1: none left): slot-row products claim from their XCD's
+  // range first, then from the other XCDs' (which run at different clocks)
+  auto claim_next = [&]() -> int {
+    if (kWgrad) {
+      const int p = stride + atomicAdd(counters, 1);
+      return p < total ? p : -1;
+    }
+    const int X = min(8, (int)gridDim.x);
+    for (int k = 0; k < X; ++k) {
+      const int y = x + k < X ? x + k : x + k - X;
+      const int s0 = (int)((long long)total * y / X), s1 = (int)((long long)total * (y + 1) / X);
+      const int p = s0 + ((int)gridDim.x - y + X - 1) / X + atomicAdd(counters + y, 1);
+      if (p < s1) return p;
+    }
+    return -1;
+  };
 
   BtTile cur = bt_tile_of<G>(a, s_tab, V, L);
   uint32_t off[kBtNI];
@@ -738,7 +752,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
     for (int i = 0; i < kBtNI; ++i) dma16(ld.base, off[i], w + i * 1024, nrec);
   }
   for (int it = 0;; ++it) {
-    if (tid == 0) s_claim[it & 1] = claim_base + atomicAdd(ctr, 1);
+    if (tid == 0) s_claim[it & 1] = claim_next();
     f32x16 acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -746,7 +760,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    int Ln = end;
+    int Ln = -1;
     BtTile nxt = cur;
     bool pre = false;  // the next tile's first k-step was issued under this tile
     if (cur.steps == 0) {
@@ -754,7 +768,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
       // previous tile before the slot is loaded again)
       pipe_sync();
       Ln = uni(s_claim[it & 1]);
-      if (G != BT_AC && Ln < end) {
+      if (G != BT_AC && Ln >= 0) {
         nxt = bt_tile_of<G>(a, s_tab, V, Ln);
         ld = bt_prepare<G>(a, nxt, wave, lane, off);
         pre = true;
@@ -775,7 +789,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
         Ln = uni(s_claim[it & 1]);
         nrec = 0;
         db = ld.base;
-        if (G != BT_AC && Ln < end) {
+        if (G != BT_AC && Ln >= 0) {
           nxt = bt_tile_of<G>(a, s_tab, V, Ln);
           ld = bt_prepare<G>(a, nxt, wave, lane, off);
           db = ld.base;
@@ -788,7 +802,7 @@ __global__ __launch_bounds__(kBtThreads, 1) void bt_gemm_kernel(BwdArgs a,
     if (G == BT_AC) pipe_sync();  // the ring is free for the staged epilogue
     bt_epilogue<G>(a, cur, wm, wn, lane, acc, lds0, lds1, s_gate, s_ds);
     ph += cur.steps;
-    if (Ln >= end) break;
+    if (Ln < 0) break;
     if (!pre) {
       // AC: its epilogue staged through the ring, so the next tile's first
       // k-step is loaded only now (the zero loads of the last k-step landed
