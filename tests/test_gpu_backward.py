@@ -131,3 +131,13 @@ def test_layer_backward_generic_kernels_bf16(name, monkeypatch):
     up = Uploaded(small_inputs(name))
     out, idx, gate = run_backward(up)
     check_gradients(up.w, out, reference(up, idx, gate))
+
+
+@pytest.mark.timeout(600)
+def test_layer_backward_2b_full():
+    """The 2B-shaped layer (T=4096, d=1280, 63 routed + 1 shared experts, top-7,
+    I=896, bf16): a routed-expert count that is not a power of two and an n-tile
+    count of 7; every gradient element against the float64 oracle."""
+    up = Uploaded(moe_inputs.make("moe2b_bf16"))
+    out, idx, gate = run_backward(up)
+    check_gradients(up.w, out, reference(up, idx, gate))
