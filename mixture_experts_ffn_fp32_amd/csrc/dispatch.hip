@@ -64,7 +64,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
                                                              int ntiles, int N, int NP2,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ tile_base) {
+                                                             int32_t* __restrict__ tile_base,
+                                                             TileTableOut tt) {
   __shared__ int csum[1024];     // [g][e] chunk sums, later chunk bases
   __shared__ int s_off[257];
   const int tid = threadIdx.x;
@@ -106,6 +107,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   }
   __syncthreads();
   for (int i = tid; i <= N; i += 1024) offsets[i] = s_off[i];
+  if (tid < 64 && tt.tiles1 != nullptr) tile_tables_wave(s_off, N, s_off[N], tt);
   if (e < N) {
     int run = s_off[e] + csum[tid];
     for (int tl = lo; tl < hi; ++tl) {
@@ -135,7 +137,8 @@ __global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __res
                                                             int T, int N, int K,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ sorted_pair) {
+                                                            int32_t* __restrict__ sorted_pair,
+                                                            TileTableOut tt) {
   __shared__ unsigned long long mask[256];
   __shared__ int s_off[257];
   const int lane = threadIdx.x;
@@ -160,8 +163,12 @@ __global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __res
     }
     carry += __shfl(inc, 63);
   }
-  if (lane == 0) offsets[N] = carry;
+  if (lane == 0) {
+    offsets[N] = carry;
+    s_off[N] = carry;
+  }
   __syncthreads();
+  if (tt.tiles1 != nullptr) tile_tables_wave(s_off, N, carry, tt);
   if (lane < T) {
     const unsigned long long below = bit - 1ull;
     for (int k = 0; k < K; ++k) {
@@ -175,8 +182,9 @@ __global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __res
 }  // namespace
 
 hipError_t launch_dispatch_small(const int32_t* idx, int T, int N, int K, int32_t* counts,
-                                 int32_t* offsets, int32_t* sorted_pair, hipStream_t stream) {
-  dispatch_small_kernel<<<1, 64, 0, stream>>>(idx, T, N, K, counts, offsets, sorted_pair);
+                                 int32_t* offsets, int32_t* sorted_pair, const TileTableOut& tt,
+                                 hipStream_t stream) {
+  dispatch_small_kernel<<<1, 64, 0, stream>>>(idx, T, N, K, counts, offsets, sorted_pair, tt);
   return hipGetLastError();
 }
 
@@ -188,11 +196,12 @@ hipError_t launch_tile_rank(const int32_t* idx, int T, int N, int K, int32_t* ti
 }
 
 hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, int32_t* counts,
-                                int32_t* offsets, int32_t* tile_base, hipStream_t stream) {
+                                int32_t* offsets, int32_t* tile_base, const TileTableOut& tt,
+                                hipStream_t stream) {
   int np2 = 1;
   while (np2 < N) np2 <<= 1;
   dispatch_scan_kernel<<<1, 1024, 0, stream>>>(tile_counts, ntiles, N, np2, counts, offsets,
-                                               tile_base);
+                                               tile_base, tt);
   return hipGetLastError();
 }
 

@@ -53,43 +53,10 @@ __device__ __forceinline__ int xcd_swizzle(int b, int G) {
   return x * q + min(x, r) + (b >> 3);
 }
 
-// Tile tables of both GEMMs from the dispatch offsets (one wavefront).
+// Tile tables of both GEMMs from caller-given dispatch offsets (one wavefront).
 __global__ __launch_bounds__(64) void tile_table_kernel(const int32_t* __restrict__ offsets,
-                                                        int N, int K_s, int T, int TK, int bm1,
-                                                        int bm2, int32_t* __restrict__ tiles1,
-                                                        int32_t* __restrict__ tiles2,
-                                                        int32_t* __restrict__ counters) {
-  const int lane = threadIdx.x;
-  if (lane < 16) counters[lane] = 0;  // the persistent GEMMs' tile claims
-  for (int which = 0; which < 2; ++which) {
-    const int V = which == 0 ? N + K_s : N + (K_s > 0 ? 1 : 0);
-    const int bm = which == 0 ? bm1 : bm2;
-    int32_t* out = which == 0 ? tiles1 : tiles2;
-    int carry = 0;
-    for (int b = 0; b < V; b += 64) {
-      const int v = b + lane;
-      int mt = 0;
-      if (v < V) {
-        int rows;
-        if (v < N) {
-          const int lo = min(max(offsets[v], 0), TK), hi = min(max(offsets[v + 1], lo), TK);
-          rows = hi - lo;
-        } else {
-          rows = T;
-        }
-        mt = (rows + bm - 1) / bm;
-      }
-      int inc = mt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-      }
-      if (v < V) out[v] = carry + inc - mt;
-      carry += __shfl(inc, 63);
-    }
-    if (lane == 0) out[V] = carry;
-  }
+                                                        int N, int TK, TileTableOut o) {
+  tile_tables_wave(offsets, N, TK, o);
 }
 
 // ---------------------------------------------------------------- shared pieces
@@ -1147,11 +1114,15 @@ hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
 
 int expert_tile_table_ints(int N, int K_s) { return (N + K_s + 1) + (N + 2) + 16; }
 
-hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream) {
+TileTableOut expert_tile_tables(int dtype, const ExpertArgs& a) {
   const int es = dtype == 1 ? 2 : 4;
-  tile_table_kernel<<<1, 64, 0, stream>>>(a.offsets, a.N, a.K_s, a.T, a.T * a.K,
-                                          shape1(a, es).bm(), shape2(a, es).bm(), a.tiles1,
-                                          a.tiles2, a.counters);
+  return TileTableOut{a.tiles1, a.tiles2, a.counters, a.K_s, a.T, shape1(a, es).bm(),
+                      shape2(a, es).bm()};
+}
+
+hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream) {
+  tile_table_kernel<<<1, 64, 0, stream>>>(a.offsets, a.N, a.T * a.K,
+                                          expert_tile_tables(dtype, a));
   return hipGetLastError();
 }
 

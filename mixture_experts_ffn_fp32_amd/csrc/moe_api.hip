@@ -167,13 +167,16 @@ struct StageScope {
 };
 
 // ---------------------------------------------------------------- launches
+// tables: the grouped GEMMs' tile tables to write as well (NULL: none).
 moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* rank,
-                          int32_t* tile_counts, int32_t* tile_base, hipStream_t st) {
+                          int32_t* tile_counts, int32_t* tile_base, hipStream_t st,
+                          const moe::TileTableOut* tables = nullptr) {
   hipError_t e;
+  const moe::TileTableOut tt = tables != nullptr ? *tables : moe::TileTableOut{};
   if (T <= moe::kRankTile) {  // one tile: ranks, scan and scatter in one launch
     StageScope sc(1, st);
-    if ((e = moe::launch_dispatch_small(idx, T, N, K, counts, offsets, sorted_pair, st)) !=
+    if ((e = moe::launch_dispatch_small(idx, T, N, K, counts, offsets, sorted_pair, tt, st)) !=
         hipSuccess)
       return hip_fail(e, "dispatch launch");
     return MOE_OK;
@@ -186,7 +189,7 @@ moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* coun
   {
     StageScope sc(2, st);
     if ((e = moe::launch_dispatch_scan(tile_counts, rank_tiles(T), N, counts, offsets, tile_base,
-                                       st)) != hipSuccess)
+                                       tt, st)) != hipSuccess)
       return hip_fail(e, "dispatch scan launch");
   }
   {
@@ -197,11 +200,13 @@ moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* coun
   return MOE_OK;
 }
 
-moe_status_t run_experts(int dtype, const moe::ExpertArgs& a, hipStream_t st) {
+// tables_ready: the dispatch launch has already written the tile tables.
+moe_status_t run_experts(int dtype, const moe::ExpertArgs& a, hipStream_t st,
+                         bool tables_ready = false) {
   hipError_t e;
   {
     StageScope sc(4, st);
-    if ((e = moe::launch_tile_table(dtype, a, st)) != hipSuccess)
+    if (!tables_ready && (e = moe::launch_tile_table(dtype, a, st)) != hipSuccess)
       return hip_fail(e, "tile table launch");
     if ((e = moe::launch_gemm1(dtype, a, st)) != hipSuccess)
       return hip_fail(e, "expert GEMM1 launch");
@@ -263,10 +268,6 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
   }
   int32_t* offsets = (int32_t*)(ws + L.offsets);
   int32_t* sorted_pair = (int32_t*)(ws + L.sorted_pair);
-  if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
-                        (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
-                        (int32_t*)(ws + L.tile_base), st)) != MOE_OK)
-    return s;
   moe::ExpertArgs a{};
   a.u = u;
   a.W_routed = W_routed;
@@ -287,7 +288,12 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
   a.N = N;
   a.K = K;
   a.K_s = K_s;
-  if ((s = run_experts(dtype, a, st)) != MOE_OK) return s;
+  const moe::TileTableOut tables = moe::expert_tile_tables(dtype, a);
+  if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
+                        (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
+                        (int32_t*)(ws + L.tile_base), st, &tables)) != MOE_OK)
+    return s;
+  if ((s = run_experts(dtype, a, st, true)) != MOE_OK) return s;
   {
     StageScope sc(6, st);
     if ((e = moe::launch_combine(dtype, u, a.Y, a.Y_shared, T, d, K, K_s, h, st)) != hipSuccess)

@@ -74,14 +74,65 @@ hipError_t launch_router(int dtype, const void* u, const void* E_gate, const flo
                          int d, int N, int K, int32_t* idx, float* gate, float* scores,
                          hipStream_t stream);
 
+// Tile tables of the grouped GEMMs: per virtual expert (routed experts, then
+// the shared ones) an exclusive prefix of m-tiles of bm rows, and the
+// persistent GEMMs' 16 tile-claim counters zeroed.  GEMM1 has N + K_s virtual
+// experts of bm1 rows (a shared expert has T rows), GEMM2 N + (K_s > 0) of
+// bm2 rows (the shared experts are one virtual expert).  Either dispatch
+// launch writes them when `tiles1` is set (the forward then needs no launch
+// of its own for them).
+struct TileTableOut {
+  int32_t* tiles1;    // [N + K_s + 1]
+  int32_t* tiles2;    // [N + 2]
+  int32_t* counters;  // [16]
+  int K_s, T, bm1, bm2;
+};
+// Lanes 0..63 of one wavefront; off[0..N] are the dispatch offsets (each
+// expert's slot range clamped into [0, TK] exactly as the GEMMs clamp it).
+__device__ __forceinline__ void tile_tables_wave(const int* off, int N, int TK,
+                                                 const TileTableOut& o) {
+  const int lane = threadIdx.x & 63;
+  if (lane < 16) o.counters[lane] = 0;
+  for (int which = 0; which < 2; ++which) {
+    const int V = which == 0 ? N + o.K_s : N + (o.K_s > 0 ? 1 : 0);
+    const int bm = which == 0 ? o.bm1 : o.bm2;
+    int32_t* out = which == 0 ? o.tiles1 : o.tiles2;
+    int carry = 0;
+    for (int b = 0; b < V; b += 64) {
+      const int v = b + lane;
+      int mt = 0;
+      if (v < V) {
+        int rows = o.T;
+        if (v < N) {
+          const int lo = min(max(off[v], 0), TK), hi = min(max(off[v + 1], lo), TK);
+          rows = hi - lo;
+        }
+        mt = (rows + bm - 1) / bm;
+      }
+      int inc = mt;
+#pragma unroll
+      for (int k = 1; k < 64; k <<= 1) {
+        const int y = __shfl_up(inc, k);
+        if (lane >= k) inc += y;
+      }
+      if (v < V) out[v] = carry + inc - mt;
+      carry += __shfl(inc, 63);
+    }
+    if (lane == 0) out[V] = carry;
+  }
+}
+
 // Dispatch: per-64-token tile ranks, global scan, scatter.
 constexpr int kRankTile = 64;
 hipError_t launch_tile_rank(const int32_t* idx, int T, int N, int K, int32_t* tile_counts,
                             int32_t* rank, hipStream_t stream);
+// tt.tiles1 == NULL: no tile tables.
 hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, int32_t* counts,
-                                int32_t* offsets, int32_t* tile_base, hipStream_t stream);
+                                int32_t* offsets, int32_t* tile_base, const TileTableOut& tt,
+                                hipStream_t stream);
 hipError_t launch_dispatch_small(const int32_t* idx, int T, int N, int K, int32_t* counts,
-                                 int32_t* offsets, int32_t* sorted_pair, hipStream_t stream);
+                                 int32_t* offsets, int32_t* sorted_pair, const TileTableOut& tt,
+                                 hipStream_t stream);
 hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_base,
                           int T, int N, int K, int32_t* sorted_pair, hipStream_t stream);
 
@@ -103,6 +154,8 @@ struct ExpertArgs {
   int T, d, I, N, K, K_s;
 };
 int expert_tile_table_ints(int N, int K_s);
+// The tables' outputs and m-tile heights for these shapes (a.offsets unused).
+TileTableOut expert_tile_tables(int dtype, const ExpertArgs& a);
 hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_gemm1(int dtype, const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_gemm2(int dtype, const ExpertArgs& a, hipStream_t stream);
