@@ -227,11 +227,18 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
 
 // Small batches (decode): one block per token.  Each of the 256 threads takes
 // 16-byte chunks of the token's row and multiplies them with the same chunks
-// of every expert row (E_gate stays in L2 across the blocks); the 64 partial
-// logits of an expert group are reduced across the wavefront by a halving
-// exchange (each lane ends with one expert's sum), then across the four
-// wavefronts in LDS in a fixed order.  Softmax and top-K run on the first
-// wavefront, each lane holding experts lane, lane + 64, ...
+// of every expert row.  The token chunk is requested together with the first
+// 32 expert chunks (E_gate through a buffer descriptor, one scalar offset per
+// expert row; it stays in L2 across the blocks), so a 2048-wide bf16 row
+// needs two round trips to memory, not three.  The 64 partial logits of an
+// expert group are reduced across the wavefront by a halving exchange (each
+// lane ends with one expert's sum), then across the four wavefronts in LDS in
+// a fixed order.  Softmax and top-K work out of LDS with thread e owning
+// expert e: every thread reads all logits (broadcast reads) and reduces them
+// in the same order, so all hold the same maximum and sum; an expert's place
+// in the top-K is its rank, the number of experts with a larger score or an
+// equal score and a smaller index (the same choice as K rounds of argmax with
+// the lowest index winning ties).
 constexpr int kSmallRouterMaxT = 128;
 
 // Element q of a 16-byte chunk as float32.
@@ -239,6 +246,7 @@ __device__ __forceinline__ float chunk_elem(ElemBF16, u32x4 w, int q) {
   return __uint_as_float((q & 1) ? (w[q >> 1] & 0xffff0000u) : (w[q >> 1] << 16));
 }
 __device__ __forceinline__ float chunk_elem(ElemF32, u32x4 w, int q) { return __uint_as_float(w[q]); }
+
 
 template <class E>
 __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* __restrict__ u,
@@ -251,19 +259,21 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
   using Tp = typename E::T;
   constexpr int PC = E::kPerChunk;
   __shared__ float s_red[4][64];
-  __shared__ float s_logit[256];
+  __shared__ float s_logit[256];  // logit + bias
+  __shared__ float s_ex[256];     // exp(logit - max)
+  __shared__ float s_p[256];      // scores
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = d / PC;  // 16-byte chunks per row
+  const int row_bytes = d * (int)sizeof(Tp);
   const Tp* ur = u + (size_t)t * d;
+  const __amdgpu_buffer_rsrc_t eg =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Eg, (short)0, N * row_bytes, 0x00020000);
   for (int eb = 0; eb < N; eb += 64) {
     float part[64];
 #pragma unroll
     for (int i = 0; i < 64; ++i) part[i] = 0.f;
     for (int c = tid; c < nch; c += 256) {
-      const u32x4 xu = *(const u32x4*)(ur + c * PC);
       float x[PC];
-#pragma unroll
-      for (int q = 0; q < PC; ++q) x[q] = chunk_elem(E{}, xu, q);
       // 32 expert chunks in flight per batch
 #pragma unroll
       for (int ib = 0; ib < 64; ib += 32) {
@@ -271,7 +281,17 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           const int e = min(eb + ib + i, N - 1);  // experts past N: a valid row, never used
-          w[i] = *(const u32x4*)(Eg + (size_t)e * d + c * PC);
+          w[i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         eg, c * 16, __builtin_amdgcn_readfirstlane(e * row_bytes), 0));
+        }
+        u32x4 xu;
+        if (ib == 0) xu = *(const u32x4*)(ur + c * PC);  // the token chunk, with the first batch
+        // every load of the batch is issued before the first wait
+        __builtin_amdgcn_sched_barrier(0);
+        if (ib == 0) {
+#pragma unroll
+          for (int q = 0; q < PC; ++q) x[q] = chunk_elem(E{}, xu, q);
         }
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
@@ -299,60 +319,38 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
     s_red[wave][lane] = part[0];
     __syncthreads();
     if (wave == 0 && eb + lane < N)
-      s_logit[eb + lane] = ((s_red[0][lane] + s_red[1][lane]) + s_red[2][lane]) + s_red[3][lane];
+      s_logit[eb + lane] =
+          (((s_red[0][lane] + s_red[1][lane]) + s_red[2][lane]) + s_red[3][lane]) +
+          (bias ? bias[eb + lane] : 0.f);
     __syncthreads();
   }
-  if (wave != 0) return;
-  float v[4];
+  // softmax: the maximum and the sum in expert order, the same in every thread
   float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < N ? s_logit[e] + (bias ? bias[e] : 0.f) : -INFINITY;
-    m = fmaxf(m, v[j]);
+  for (int e = 0; e < N; ++e) m = fmaxf(m, s_logit[e]);
+  float ex = 0.f;
+  if (tid < N) {
+    ex = expf(s_logit[tid] - m);
+    s_ex[tid] = ex;
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __syncthreads();
   float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < N ? expf(v[j] - m) : 0.f;
-    sum += v[j];
+  for (int e = 0; e < N; ++e) sum += s_ex[e];
+  float sc = 0.f;
+  if (tid < N) {
+    sc = ex / sum;
+    s_p[tid] = sc;
+    if (scores != nullptr) scores[(size_t)t * N + tid] = sc;
   }
-  // butterfly: every lane ends with the same bits
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < N ? v[j] / sum : -2.f;  // scores are >= 0; -2 marks padding
-    if (scores != nullptr && e < N) scores[(size_t)t * N + e] = v[j];
-  }
-  for (int k = 0; k < K; ++k) {
-    float bv = -1.f;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)  // ascending expert id within the lane
-      if (v[j] > bv) {
-        bv = v[j];
-        bi = lane + 64 * j;
-      }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+  __syncthreads();
+  if (tid < N) {
+    int rank = 0;
+    for (int e = 0; e < N; ++e) {
+      const float o = s_p[e];
+      rank += (o > sc || (o == sc && e < tid)) ? 1 : 0;
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == bi) v[j] = -1.f;  // taken (-1 is below every score)
-    if (lane == 0) {
-      idx[(size_t)t * K + k] = bi;
-      gate[(size_t)t * K + k] = bv;
+    if (rank < K) {
+      idx[(size_t)t * K + rank] = tid;
+      gate[(size_t)t * K + rank] = sc;
     }
   }
 }
