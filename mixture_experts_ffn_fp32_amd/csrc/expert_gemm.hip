@@ -777,16 +777,21 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
 // x 128 B rows (GEMM1: gate and up rows of 64 columns, interleaved in runs
 // of 32; GEMM2: 128 output columns), one 128-byte k-step of every row per
 // ring slot, kStrS slots.  The block is persistent and walks its tiles as
-// one sequence of k-steps.  Wavefronts 2 and 3 only load: they keep the
-// next kStrS - 1 k-steps in flight with direct-to-LDS buffer loads, wait for
-// the oldest with an exact vmcnt (they issue nothing else), and release it
-// with a barrier.  Wavefronts 0 and 1 only compute: after each barrier they
-// multiply the released slot (each owns 64 of the 128 B rows) and, at the
-// end of a tile, write its rows.
-constexpr int kStrBM = 32, kStrBR = 128, kStrS = 6;
+// one sequence of k-steps.  Wavefronts 2..5 only load: they keep the next
+// kStrS - 1 k-steps in flight with direct-to-LDS buffer loads, wait for the
+// oldest with an exact vmcnt (they issue nothing else), and release it with a
+// barrier (four loading wavefronts issue ~1% faster than two: the loads are
+// accepted at the rate the memory system takes them, not issued late).
+// Wavefronts 0 and 1 only compute: after each barrier they multiply the
+// released slot (each owns 64 of the 128 B rows) and, at the end of a tile,
+// write its rows.
+constexpr int kStrBM = 32, kStrBR = 128, kStrS = 6, kStrLW = 4;
 constexpr int kStrRows = kStrBM + kStrBR;
 constexpr int kStrSlot = kStrRows * 128;
-constexpr int kStrNI = kStrRows / 8 / 2;  // loads per loading wavefront per k-step
+constexpr int kStrNI = kStrRows / 8 / kStrLW;  // loads per loading wavefront per k-step
+constexpr int kStrThreads = 64 * (2 + kStrLW);
+static_assert(kStrRows % (8 * kStrLW) == 0 && kStrBM % 8 == 0, "whole 8-row loads per wavefront");
+static_assert((kStrS - 2) * kStrNI < 64, "vmcnt range");
 
 template <int MODE>
 __host__ __device__ __forceinline__ int str_nt(const ExpertArgs& a) {
@@ -828,7 +833,7 @@ __device__ __forceinline__ int str_perm(int p, int total, int G, int E) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void expert_gemm_stream_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(kStrThreads, 1) void expert_gemm_stream_kernel(ExpertArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStrS * kStrSlot];
   __shared__ int s_tab[kMaxV + 1];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -845,7 +850,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_stream_kernel(ExpertArgs a
     nsteps_all += str_steps<MODE>(a, tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, str_perm(L, total, G, E)));
 
   if (wave >= 2) {
-    // ---- loading wavefronts: rows (wave - 2) * 80 .. + 79 of each slot
+    // ---- loading wavefronts: rows (wave - 2) * 8 kStrNI .. + 8 kStrNI - 1 of each slot
     const int w2 = wave - 2;
     int L = blockIdx.x, s = 0;
     Tile ti = uni(tile_of<kStrBM, (MODE == 1 ? kStrBR / 2 : kStrBR), MODE>(a, s_tab, V, str_perm(L, total, G, E)));
@@ -1082,7 +1087,7 @@ hipError_t launch_stream(const ExpertArgs& a, hipStream_t st) {
   long long g = grid_tiles(a, kStrBM, str_nt<MODE>(a), MODE);
   if (g <= 0) return hipSuccess;
   g = std::min<long long>(g, (long long)cu_count());  // persistent: one block per CU
-  expert_gemm_stream_kernel<MODE><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
+  expert_gemm_stream_kernel<MODE><<<dim3((unsigned)g), dim3(kStrThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
