@@ -1001,7 +1001,9 @@ struct Shape {
 
 // Few tokens per expert (decode-sized batches): short M tiles, wide N tiles,
 // so every CU streams a large weight slab.
-bool small_m(const ExpertArgs& a) { return (long long)a.T * a.K < 64LL * a.N; }
+bool small_m(const ExpertArgs& a) {
+  return (long long)a.T * a.K < 64LL * (a.sel_N > 0 ? a.sel_N : a.N);
+}
 
 // MOE_GEMM_VARIANT=reg forces the register-staged kernel (read once; for tuning runs).
 bool force_reg() {

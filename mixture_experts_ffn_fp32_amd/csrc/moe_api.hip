@@ -82,7 +82,7 @@ moe_status_t hip_fail(hipError_t e, const char* what) {
 
 // ---------------------------------------------------------------- workspace
 struct Layout {
-  size_t idx, gate, rank, tile_counts, tile_base, counts, offsets, sorted_pair, tiles;
+  size_t idx, gate, rank, tile_counts, tile_base, counts, offsets, sorted_pair, tiles, tiles_side;
   size_t H_routed, H_shared, Y, Y_shared, total;
 };
 
@@ -107,6 +107,7 @@ Layout make_layout(int T, int d, int I, int N, int K, int K_s, int dtype) {
   L.offsets = take((size_t)(N + 1) * 4);
   L.sorted_pair = take(TK * 4);
   L.tiles = take((size_t)moe::expert_tile_table_ints(N, K_s) * 4);
+  L.tiles_side = take((size_t)moe::expert_tile_table_ints(0, K_s) * 4);
   L.H_routed = take(TK * I * es);
   L.H_shared = take((size_t)T * K_s * I * es);
   L.Y = take(TK * d * es);
@@ -165,6 +166,44 @@ struct StageScope {
     g_timing.recs.push_back({stage, a, b});
   }
 };
+
+// ---------------------------------------------------------------- shared experts beside the routing
+// In decode-sized batches the router and the dispatch are latency-bound
+// launches during which HBM is idle, and the shared experts need no routing:
+// their two GEMMs run on a second stream of the library's own (default
+// priority) meanwhile, forked from and joined into the caller's stream with
+// events.  One set per device; the enqueue sequence holds a lock, so calls
+// from several host threads keep each fork and join paired.
+constexpr int kSideMaxT = 128;
+struct Side {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+Side g_side[64];
+
+// MOE_SHARED_SIDE=0 keeps the shared experts in the routed GEMM launches
+// (read on every call).
+bool side_enabled() {
+  const char* e = getenv("MOE_SHARED_SIDE");
+  return !(e != nullptr && e[0] == '0');
+}
+
+// Caller holds g_side_mu.
+hipError_t side_of_device(Side** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  Side& sd = g_side[dev];
+  if (sd.st == nullptr) {
+    if ((e = hipStreamCreateWithFlags(&sd.st, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &sd;
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------- launches
 // tables: the grouped GEMMs' tile tables to write as well (NULL: none).
@@ -260,12 +299,6 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
   int32_t* idx = (int32_t*)(ws + L.idx);
   float* gate = (float*)(ws + L.gate);
   hipError_t e;
-  {
-    StageScope sc(0, st);
-    if ((e = moe::launch_router(dtype, u, E_gate, gate_bias, T, d, N, K, idx, gate, nullptr, st)) !=
-        hipSuccess)
-      return hip_fail(e, "router launch");
-  }
   int32_t* offsets = (int32_t*)(ws + L.offsets);
   int32_t* sorted_pair = (int32_t*)(ws + L.sorted_pair);
   moe::ExpertArgs a{};
@@ -288,12 +321,45 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
   a.N = N;
   a.K = K;
   a.K_s = K_s;
-  const moe::TileTableOut tables = moe::expert_tile_tables(dtype, a);
+  // decode-sized batches: the shared experts on the side stream, the routed
+  // ones (a K_s = 0 view of the same buffers) after the dispatch
+  const bool side = K_s > 0 && T <= kSideMaxT && side_enabled();
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  Side* sd = nullptr;
+  moe::ExpertArgs ar = a;
+  if (side) {
+    side_lock.lock();
+    if ((e = side_of_device(&sd)) != hipSuccess) return hip_fail(e, "side stream");
+    moe::ExpertArgs as = a;
+    as.N = 0;
+    as.sel_N = N;
+    as.tiles1 = (int32_t*)(ws + L.tiles_side);
+    as.tiles2 = as.tiles1 + (K_s + 1);
+    as.counters = as.tiles2 + 2;
+    if ((e = hipEventRecord(sd->fork, st)) != hipSuccess ||
+        (e = hipStreamWaitEvent(sd->st, sd->fork, 0)) != hipSuccess ||
+        (e = moe::launch_tile_table(dtype, as, sd->st)) != hipSuccess ||
+        (e = moe::launch_gemm1(dtype, as, sd->st)) != hipSuccess ||
+        (e = moe::launch_gemm2(dtype, as, sd->st)) != hipSuccess ||
+        (e = hipEventRecord(sd->join, sd->st)) != hipSuccess)
+      return hip_fail(e, "shared-expert launches");
+    ar.K_s = 0;
+  }
+  {
+    StageScope sc(0, st);
+    if ((e = moe::launch_router(dtype, u, E_gate, gate_bias, T, d, N, K, idx, gate, nullptr, st)) !=
+        hipSuccess)
+      return hip_fail(e, "router launch");
+  }
+  const moe::TileTableOut tables = moe::expert_tile_tables(dtype, ar);
   if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
                         (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
                         (int32_t*)(ws + L.tile_base), st, &tables)) != MOE_OK)
     return s;
-  if ((s = run_experts(dtype, a, st, true)) != MOE_OK) return s;
+  if ((s = run_experts(dtype, ar, st, true)) != MOE_OK) return s;
+  if (side && (e = hipStreamWaitEvent(st, sd->join, 0)) != hipSuccess)
+    return hip_fail(e, "shared-expert join");
+  if (side) side_lock.unlock();
   {
     StageScope sc(6, st);
     if ((e = moe::launch_combine(dtype, u, a.Y, a.Y_shared, T, d, K, K_s, h, st)) != hipSuccess)

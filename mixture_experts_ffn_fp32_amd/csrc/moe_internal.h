@@ -152,6 +152,9 @@ struct ExpertArgs {
   int32_t* tiles2;             // [N+2]     m-tile prefix for GEMM2
   int32_t* counters;           // [16]      tile claims per XCD (GEMM1, GEMM2), zeroed per launch
   int T, d, I, N, K, K_s;
+  // N that picks the kernels (0: N).  A launch over the shared experts alone
+  // (N = 0) keeps the choice the whole layer would make.
+  int sel_N;
 };
 int expert_tile_table_ints(int N, int K_s);
 // The tables' outputs and m-tile heights for these shapes (a.offsets unused).
