@@ -993,10 +993,13 @@ __global__ __launch_bounds__(kStrThreads, 1) void expert_gemm_stream_kernel(Expe
 
 // Kernel choice.  kind 0: register-staged kernel with wavefronts WM x WN and
 // 32x32 fragments FM x FN per wavefront; kind 1: the pipelined LDS-DMA
-// kernel; kind 2: the weight-streaming kernel (bf16, decode-sized batches).
+// kernel; kinds 2 and 3: the weight-streaming kernels (bf16, decode-sized
+// batches; 3: 512-byte runs with the token rows held in LDS, where they fit).
 struct Shape {
   int kind, WM, WN, FM, FN;
-  int bm() const { return kind == 1 ? kPipeBM : kind == 2 ? kStrBM : WM * FM * 32; }
+  int bm() const {
+    return kind == 1 ? kPipeBM : kind == 2 ? kStrBM : kind == 3 ? stream_long_rows() : WM * FM * 32;
+  }
 };
 
 // Few tokens per expert (decode-sized batches): short M tiles, wide N tiles,
@@ -1029,13 +1032,21 @@ int pipe_waves() {
 bool pipe_ok1(const ExpertArgs& a, int es) { return (a.d * es) % 128 == 0 && a.I % 64 == 0; }
 bool pipe_ok2(const ExpertArgs& a, int es) { return (a.I * es) % 128 == 0 && a.d % 64 == 0; }
 
+// MOE_STREAM=short keeps the 128-byte-run streaming kernel (read on every call).
+bool stream_long(int mode, const ExpertArgs& a) {
+  const char* e = getenv("MOE_STREAM");
+  return !(e != nullptr && !strcmp(e, "short")) && stream_long_ok(mode, a);
+}
+
 Shape shape1(const ExpertArgs& a, int es) {
-  if (small_m(a) && es == 2 && !force_reg()) return Shape{2, 0, 0, 0, 0};
+  if (small_m(a) && es == 2 && !force_reg())
+    return Shape{stream_long(1, a) ? 3 : 2, 0, 0, 0, 0};
   if (small_m(a)) return a.I % 128 == 0 ? Shape{0, 1, 4, 1, 2} : Shape{0, 2, 2, 1, 2};
   if (!force_reg() && pipe_ok1(a, es)) return Shape{1, 4, 2, 2, 4};
   return Shape{0, 2, 2, 2, 2};
 }
 Shape shape2(const ExpertArgs& a, int es) {
+  if (small_m(a) && es == 2 && !force_reg() && stream_long(2, a)) return Shape{3, 0, 0, 0, 0};
   if (small_m(a) && es == 2 && !force_reg() && a.d % kStrBR == 0) return Shape{2, 0, 0, 0, 0};
   if (small_m(a)) return a.d % 256 == 0 ? Shape{0, 1, 4, 1, 2} : Shape{0, 2, 2, 1, 1};
   if (!force_reg() && pipe_ok2(a, es)) return Shape{1, 4, 2, 2, 4};
@@ -1097,8 +1108,10 @@ template <class E, int MODE>
 hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
   const int es = (int)sizeof(typename E::T);
   const Shape s = MODE == 1 ? shape1(a, es) : shape2(a, es);
-  if constexpr (std::is_same<E, ElemBF16>::value)
+  if constexpr (std::is_same<E, ElemBF16>::value) {
     if (s.kind == 2) return launch_stream<MODE>(a, st);
+    if (s.kind == 3) return launch_stream_long(MODE, a, cu_count(), st);
+  }
   if (s.kind == 1) {
     // float32 keeps eight wavefronts (its four-wavefront build spills)
     if constexpr (std::is_same<E, ElemF32>::value)

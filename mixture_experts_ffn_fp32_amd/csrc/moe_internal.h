@@ -156,6 +156,11 @@ struct ExpertArgs {
   // (N = 0) keeps the choice the whole layer would make.
   int sel_N;
 };
+// Weight streaming with 512-byte runs per weight row (expert_stream.hip):
+// whether a launch of GEMM `mode` fits it, its m-tile height, and the launch.
+bool stream_long_ok(int mode, const ExpertArgs& a);
+int stream_long_rows();
+hipError_t launch_stream_long(int mode, const ExpertArgs& a, int cus, hipStream_t st);
 int expert_tile_table_ints(int N, int K_s);
 // The tables' outputs and m-tile heights for these shapes (a.offsets unused).
 TileTableOut expert_tile_tables(int dtype, const ExpertArgs& a);
