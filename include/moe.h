@@ -76,12 +76,12 @@ moe_status_t moe_workspace_size(int T, int d, int I, int N, int K, int K_s, int 
  * Routing ties are broken towards the lower expert index; each token's K
  * routed contributions are summed in descending-score order, after the
  * shared experts' sum, in float32, and h is rounded once.
- * With K_s > 0 and T <= 128 the shared experts' GEMMs run on a stream the
- * library owns (one per device, default priority), forked from `stream` by
- * an event before the router and joined back into it before the combine:
- * everything the call does is still ordered on `stream` for the caller, and
- * the result is the same bits as with MOE_SHARED_SIDE=0 in the environment,
- * which keeps them on `stream`. */
+ * With MOE_SHARED_SIDE=1 in the environment, K_s > 0 and T <= 128, the
+ * shared experts' GEMMs run on a stream the library owns (one per device,
+ * default priority), forked from `stream` by an event before the router and
+ * joined back into it before the combine: everything the call does is still
+ * ordered on `stream` for the caller, and the result is the same bits as
+ * without it, which keeps them on `stream`. */
 moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_routed,
                                const void* W_shared, int N, int K, int K_s, int T, int d,
                                int I, int dtype, const float* gate_bias, void* h,

@@ -167,15 +167,16 @@ def test_deterministic_and_chunk_invariant(small):
 
 @pytest.mark.parametrize("name", ["one_token_bf16", "k_equals_n_f32", "decode_n256_bf16"])
 def test_shared_experts_beside_routing_same_bits(name, monkeypatch):
-    """Batches of at most 128 tokens run the shared experts' GEMMs on a second
-    stream while the router and the dispatch run; the result must be the same
-    bits as with every expert in the same launches (MOE_SHARED_SIDE=0): each
-    tile is the same arithmetic either way."""
+    """With MOE_SHARED_SIDE=1, batches of at most 128 tokens run the shared
+    experts' GEMMs on a second stream while the router and the dispatch run;
+    the result must be the same bits as with every expert in the same
+    launches (the default): each tile is the same arithmetic either way."""
     up = Uploaded(small_inputs(name))
     w = up.w
     assert w.K_s > 0 and w.T <= 128
     say(f"shared experts beside routing {w.name}")
     args = (up.E, up.W_routed, up.W_shared, w.N, w.K, w.K_s, up.bias)
+    monkeypatch.setenv("MOE_SHARED_SIDE", "1")
     h_side = mx.layer_forward(up.u, *args)
     torch.cuda.synchronize()
     monkeypatch.setenv("MOE_SHARED_SIDE", "0")
