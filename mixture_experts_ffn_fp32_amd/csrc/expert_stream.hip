@@ -15,15 +15,19 @@
 //  * a tile is (virtual expert, 16 token rows, 32 weight rows): GEMM1 the
 //    gate and up rows of 16 columns of H, GEMM2 32 columns of Y; a k-step
 //    takes 512 bytes of each weight row into one 16 KB ring slot;
-//  * a block walks a contiguous range of tiles with the weight rows fastest,
-//    so the token rows change only between (expert, 16-row) groups; the
-//    computing wavefront then loads them (16 rows x the whole contraction,
-//    at most 64 KB) into its own LDS region and waits for them;
+//  * a segment is (virtual expert, 16-row group): its token rows (16 rows x
+//    the whole contraction, at most 64 KB) are loaded into LDS once and stay
+//    there while the segment's weight-row groups stream past;
+//  * with at least as many segments as blocks, a block takes a contiguous
+//    run of whole segments; with fewer, P blocks share a segment, each
+//    taking a contiguous share of its weight-row groups;
 //  * four wavefronts only load: they keep four k-steps in flight with
 //    direct-to-LDS buffer loads, wait for the oldest with an exact vmcnt and
-//    release it with a barrier; one wavefront computes (16x16x32 bf16 MFMA,
+//    release it with a barrier; two wavefronts compute (16x16x32 bf16 MFMA,
 //    weights as the 16-row operand so a lane holds four consecutive output
-//    columns of one token) and writes each finished tile with 8-byte stores.
+//    columns of one token), each on half of every k-step's k-groups; the
+//    second hands its sums to the first through LDS, which finishes the tile
+//    with 8-byte stores.
 #include "lds_dma.h"
 #include "moe_internal.h"
 
