@@ -215,6 +215,10 @@ moe_status_t moe_layer_backward(const void* u, const void* E_gate, const void* W
  *              of at most 64 tokens runs the whole dispatch as stage 1. */
 moe_status_t moe_timing_enable(int on);
 moe_status_t moe_timing_read(double* ms_per_stage, int* launches_per_stage);
+/* Stages that get an event pair while timing is on: bit s selects stage s
+ * (default all).  Fewer events disturb the timed launches less (each pair
+ * separates back-to-back kernels on the stream). */
+moe_status_t moe_timing_stages(unsigned mask);
 
 #ifdef __cplusplus
 }

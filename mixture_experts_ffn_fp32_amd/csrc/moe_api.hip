@@ -128,6 +128,7 @@ size_t expert_ws_bytes(int N, int K_s) {
 struct Timing {
   std::mutex mu;
   bool on = false;
+  unsigned mask = ~0u;  // stages that get an event pair
   std::vector<hipEvent_t> pool;
   struct Rec {
     int stage;
@@ -154,7 +155,7 @@ struct StageScope {
   hipEvent_t a = nullptr, b = nullptr;
   StageScope(int s, hipStream_t stream) : stage(s), st(stream) {
     std::lock_guard<std::mutex> g(g_timing.mu);
-    if (!g_timing.on) return;
+    if (!g_timing.on || !((g_timing.mask >> s) & 1u)) return;
     a = g_timing.get();
     b = g_timing.get();
     if (a && b) (void)hipEventRecord(a, st);
@@ -730,6 +731,12 @@ moe_status_t moe_balance_stats(const float* scores, const int32_t* idx, int T, i
 moe_status_t moe_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_timing.mu);
   g_timing.on = on != 0;
+  return ok();
+}
+
+moe_status_t moe_timing_stages(unsigned mask) {
+  std::lock_guard<std::mutex> g(g_timing.mu);
+  g_timing.mask = mask;
   return ok();
 }
 

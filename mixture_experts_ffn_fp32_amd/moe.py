@@ -24,7 +24,7 @@ EXPORTED = ("moe_last_error", "moe_workspace_size", "moe_layer_forward", "moe_ro
             "moe_dispatch_workspace_size", "moe_dispatch", "moe_expert_ffn_workspace_size",
             "moe_expert_ffn", "moe_combine", "moe_balance_workspace_size", "moe_balance_stats",
             "moe_backward_workspace_size", "moe_layer_backward", "moe_timing_enable",
-            "moe_timing_read")
+            "moe_timing_read", "moe_timing_stages")
 
 
 class MoEError(RuntimeError):
@@ -66,6 +66,7 @@ def load_library(path: str = LIB_PATH):
                                sz, vp],
         "moe_timing_enable": [i],
         "moe_timing_read": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)],
+        "moe_timing_stages": [ctypes.c_uint],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -280,8 +281,12 @@ def balance_stats(scores, idx, K: int, group_of=None, alpha1: float = 1.0, alpha
     return res
 
 
-def timing_enable(on: bool = True):
-    _check(load_library().moe_timing_enable(1 if on else 0))
+def timing_enable(on: bool = True, stages=None):
+    """Per-stage event timing on or off; `stages` (names) limits it to those stages."""
+    L = load_library()
+    mask = 0xFFFFFFFF if stages is None else sum(1 << STAGE_NAMES.index(s) for s in stages)
+    _check(L.moe_timing_stages(mask))
+    _check(L.moe_timing_enable(1 if on else 0))
 
 
 def timing_read():
