@@ -274,6 +274,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
     for (int i = 0; i < 64; ++i) part[i] = 0.f;
     for (int c = tid; c < nch; c += 256) {
       float x[PC];
+      u32x4 xw;  // the token chunk's raw words (bf16: four bf16 pairs)
       // 32 expert chunks in flight per batch
 #pragma unroll
       for (int ib = 0; ib < 64; ib += 32) {
@@ -290,15 +291,34 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
         // every load of the batch is issued before the first wait
         __builtin_amdgcn_sched_barrier(0);
         if (ib == 0) {
+          xw = xu;
 #pragma unroll
           for (int q = 0; q < PC; ++q) x[q] = chunk_elem(E{}, xu, q);
         }
+        if constexpr (PC == 8) {
+          // bf16: a two-term dot product per instruction straight from the
+          // packed pairs (products exact in float32, summed in float32).  The
+          // words go through plain arrays: a bit cast of a subscripted vector
+          // element compiles to element 0 for every subscript.
+          const uint32_t xs[4] = {xw.x, xw.y, xw.z, xw.w};
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          float acc = 0.f;
+          for (int i = 0; i < 32; ++i) {
+            const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+            float acc = 0.f;
 #pragma unroll
-          for (int q = 0; q < PC; ++q) acc += x[q] * chunk_elem(E{}, w[i], q);
-          part[ib + i] += acc;
+            for (int q = 0; q < 4; ++q)
+              acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xs[q]),
+                                                    __builtin_bit_cast(bf16x2, ws[q]), acc, false);
+            part[ib + i] += acc;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < PC; ++q) acc += x[q] * chunk_elem(E{}, w[i], q);
+            part[ib + i] += acc;
+          }
         }
       }
     }
