@@ -147,6 +147,31 @@ def test_layer_forward(small):
             w.name)
 
 
+@pytest.mark.parametrize("name", ["one_token_bf16", "n256_bf16", "decode_n256_bf16",
+                                  "gran_m8_ks1_bf16"])
+def test_layer_forward_short_run_streaming(name, monkeypatch):
+    """Decode-sized bf16 batches take the long-run streaming GEMMs by default;
+    MOE_STREAM=short keeps them on the short-run streaming kernel, which must
+    match the oracle as well."""
+    up = Uploaded(small_inputs(name))
+    w = up.w
+    say(f"layer_forward MOE_STREAM=short {w.name}")
+    monkeypatch.setenv("MOE_STREAM", "short")
+    h = mx.layer_forward(up.u, up.E, up.W_routed, up.W_shared, w.N, w.K, w.K_s, up.bias)
+    idx, gate, _ = mx.route(up.u, up.E, w.K, up.bias)
+    torch.cuda.synchronize()
+    inp = up.inp
+    h_ref, info = oracle.moe_forward_tokens(inp.u_f32(), inp.E_gate_f32(), up.routed, up.shared,
+                                            w.N, w.K, w.K_s, inp.gate_bias())
+    differing, alts = check_routing(idx.cpu().numpy(), gate.cpu().numpy(), info["s"], w.K)
+    for t in differing:
+        a_idx, a_g = alts[int(t)]
+        h_ref[t] = oracle.moe_forward_given_routing(inp.u_f32()[t:t + 1], a_idx[None], a_g[None],
+                                                    up.routed, up.shared, w.K_s)[0]
+    check_h(device_f32(h), h_ref, inp.u_f32().astype(np.float64), tol_for(w), w.dtype, w.K,
+            w.name)
+
+
 def test_deterministic_and_chunk_invariant(small):
     w = small.w
     if w.T < 4:
