@@ -202,7 +202,9 @@ def near_tie_alternatives(s, K: int, eps: float = 1e-6):
 
     Returns {t: (idx_alt [K], g_alt [K])}: the top-K set with its K-th expert
     replaced by the (K+1)-th.  Either set satisfies "keep the K largest" up to
-    eps, so either is a correct routing in finite precision.
+    eps, so either is a correct routing in finite precision.  An exact tie
+    (margin 0) has one correct answer, the lower index (exactly K gates are
+    non-zero, [DSMoE] A3), so it has no alternative.
     """
     s = _f64(s)
     idx, g, margin = top_k_gates(s, K)
@@ -210,7 +212,7 @@ def near_tie_alternatives(s, K: int, eps: float = 1e-6):
     if K >= s.shape[1]:
         return out
     order = np.argsort(-s, axis=1, kind="stable")
-    for t in np.nonzero(margin <= eps)[0]:
+    for t in np.nonzero((margin > 0) & (margin <= eps))[0]:
         alt = idx[t].copy()
         alt[K - 1] = order[t, K]
         out[int(t)] = (alt, s[t, alt])

@@ -54,6 +54,79 @@ def test_route_small_batch_kernels_agree(name, monkeypatch):
         check_routing(idx.cpu().numpy(), gate.cpu().numpy(), s_ref, w.K)
 
 
+def _tie_inputs(T, d, N, K, pattern, dtype, with_bias, seed):
+    """Router inputs whose scores have planted EXACT ties: every token ranks the experts in
+    the same order (expert perm[r] at rank r, logit levels one unit apart), and the experts
+    of one tie group have bit-identical centroid rows (and biases), so their logits are
+    equal on both sides whatever the token.  `pattern` lists the rank groups that tie."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(N)
+    level = np.zeros(N, dtype=np.float32)
+    noise = rng.standard_normal((N, d - 1)).astype(np.float32) * 0.01
+    bias = rng.standard_normal(N).astype(np.float32) * 0.25
+    lead = {}
+    for grp in pattern:
+        for r in grp[1:]:
+            lead[r] = grp[0]
+    for r in range(N):
+        level[perm[r]] = float(N - lead.get(r, r))
+        noise[perm[r]] = noise[perm[lead.get(r, r)]]
+        bias[perm[r]] = bias[perm[lead.get(r, r)]]
+    E = np.concatenate([level[:, None], noise], axis=1)
+    u = rng.standard_normal((T, d)).astype(np.float32) * 0.5
+    u[:, 0] = 2.0 + 0.25 * rng.random(T).astype(np.float32)
+    if dtype == "bf16":
+        E = moe_inputs.bf16_bits_to_f32(moe_inputs.f32_to_bf16_bits(E))
+        u = moe_inputs.bf16_bits_to_f32(moe_inputs.f32_to_bf16_bits(u))
+    tie_sets = [sorted(int(perm[r]) for r in grp) for grp in pattern]
+    return u, E, (bias if with_bias else None), tie_sets
+
+
+TIE_CASES = {
+    # (T, d, N, K, tie groups of ranks)
+    "boundary_pair": (100, 128, 16, 4, [(3, 4), (0, 1)]),
+    "boundary_triple": (300, 256, 64, 6, [(4, 5, 6)]),
+    "boundary_pair_tiled": (300, 128, 16, 4, [(3, 4)]),
+    "top1_pair": (70, 64, 8, 1, [(0, 1)]),
+    "decode_n256_pair": (64, 256, 256, 8, [(7, 8), (2, 3, 4)]),
+}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", sorted(TIE_CASES))
+@pytest.mark.parametrize("router", ["auto", "tiled"])
+def test_route_exact_ties_go_to_lower_index(case, dtype, router, monkeypatch):
+    """Exact ties at the K-th / (K+1)-th rank (and inside the top-K) are broken towards
+    the lower expert index, bit-exact, by both router kernels (one block per token for
+    T <= 128, the tiled kernel otherwise or with MOE_ROUTER_SMALL=0)."""
+    T, d, N, K, pattern = TIE_CASES[case]
+    for with_bias in (False, True):
+        u, E, bias, tie_sets = _tie_inputs(T, d, N, K, pattern, dtype, with_bias,
+                                           seed=4000 + sorted(TIE_CASES).index(case))
+        s_ref = oracle.affinity_scores(u, E, bias)
+        idx_ref, g_ref, margin = oracle.top_k_gates(s_ref, K)
+        boundary = any(K - 1 in grp and K in grp for grp in pattern)
+        if boundary:
+            assert np.all(margin == 0.0)     # the planted tie really is exact
+        if router == "tiled":
+            monkeypatch.setenv("MOE_ROUTER_SMALL", "0")
+        say(f"route ties {case} {dtype} bias={with_bias} router={router} T={T} N={N} K={K}")
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        ud = torch.from_numpy(u).to("cuda", tdt)
+        Ed = torch.from_numpy(E).to("cuda", tdt)
+        bd = None if bias is None else torch.from_numpy(bias).cuda()
+        idx, gate, scores = mx.route(ud, Ed, K, bd, want_scores=True)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("MOE_ROUTER_SMALL", raising=False)
+        ig = idx.cpu().numpy()
+        sc = scores.cpu().numpy()
+        for grp in tie_sets:                 # equal on the GPU too
+            assert np.all(sc[:, grp] == sc[:, grp[:1]])
+        np.testing.assert_array_equal(ig, idx_ref)   # set and order, bit-exact
+        np.testing.assert_allclose(gate.cpu().numpy(), g_ref, rtol=1e-5)
+        check_routing(ig, gate.cpu().numpy(), s_ref, K)
+
+
 def test_dispatch(small):
     w = small.w
     s_ref = oracle.affinity_scores(small.inp.u_f32(), small.inp.E_gate_f32(), small.inp.gate_bias())

@@ -33,6 +33,10 @@ MUTATIONS = {
     "unstable_permutation": ('sorted_pair = np.argsort(flat, kind="stable")',
                              'sorted_pair = np.argsort(flat, kind="stable")[::-1]'),
     "margin_wrong_neighbour": ('margin = g[:, K - 1] - nxt', 'margin = g[:, 0] - nxt'),
+    "device_f_sum_not_mean": ('fg = np.array([f[list(gr)].mean() for gr in groups])',
+                              'fg = np.array([f[list(gr)].sum() for gr in groups])'),
+    "device_P_mean_not_sum": ('Pg = np.array([P[list(gr)].sum() for gr in groups])',
+                              'Pg = np.array([P[list(gr)].mean() for gr in groups])'),
 }
 
 

@@ -374,6 +374,32 @@ def test_balance_statistics_closed_forms():
     np.testing.assert_allclose(st3["f"], [N / K] * K + [0] * (N - K))
 
 
+def test_device_balance_with_multi_expert_groups():
+    """Device groups of several experts ([DSMoE] sec. 3.3 device-level loss): f'_g is the
+    MEAN of f over the group and P'_g the SUM of P over it.  Collapsed routing (every token
+    keeps experts 0, 1, 2 of N = 8) with groups {0, 1} and {2, ..., 7}, worked by hand:
+    f = (8/3, 8/3, 8/3, 0, 0, 0, 0, 0), so f'_0 = 8/3 and f'_1 = (8/3) / 6 = 4/9;
+    every token has the scores below, so P = s and P' = (0.5, 0.5);
+    L_DevBal = alpha2 * (8/3 * 0.5 + 4/9 * 0.5) = alpha2 * 14/9."""
+    T, N, K = 10, 8, 3
+    row = np.array([0.3, 0.2, 0.1, 0.1, 0.1, 0.1, 0.05, 0.05])
+    s = np.tile(row, (T, 1))
+    idx = np.tile(np.arange(K), (T, 1))
+    groups = [[0, 1], [2, 3, 4, 5, 6, 7]]
+    st = oracle.balance_statistics(s, idx, K, groups=groups, alpha1=1.0, alpha2=3.0)
+    np.testing.assert_allclose(st["f"], [8 / 3] * 3 + [0] * 5, rtol=1e-15)
+    np.testing.assert_allclose(st["f_dev"], [8 / 3, 4 / 9], rtol=1e-15)
+    np.testing.assert_allclose(st["P_dev"], [0.5, 0.5], rtol=1e-15)
+    assert st["L_DevBal"] == pytest.approx(3.0 * 14 / 9, rel=1e-15)
+    # L_ExpBal over the same batch: sum_i f_i P_i = 8/3 * (0.3 + 0.2 + 0.1) = 1.6
+    assert st["L_ExpBal"] == pytest.approx(1.6, rel=1e-15)
+    # uneven groups {0..5}, {6}, {7}: f' = (8/3 * 3 / 6, 0, 0), P' = (0.9, 0.05, 0.05)
+    st2 = oracle.balance_statistics(s, idx, K, groups=[[0, 1, 2, 3, 4, 5], [6], [7]], alpha2=1.0)
+    np.testing.assert_allclose(st2["f_dev"], [4 / 3, 0.0, 0.0], rtol=1e-15)
+    np.testing.assert_allclose(st2["P_dev"], [0.9, 0.05, 0.05], rtol=1e-15)
+    assert st2["L_DevBal"] == pytest.approx(4 / 3 * 0.9, rel=1e-15)
+
+
 def test_given_routing_equals_layer_and_identical_experts():
     # with the oracle's own routing it reproduces the layer; with identical experts it
     # gives u + shared + (sum of the supplied gates) FFN(u) for any supplied set
@@ -398,6 +424,11 @@ def test_near_tie_alternative_swaps_boundary_expert():
     assert list(alts) == [0]
     assert sorted(alts[0][0].tolist()) == [0, 1]      # expert 2 (K-th) swapped for expert 1
     assert oracle.near_tie_alternatives(s, 1) == {}
+    # an exact tie at the boundary is decided by the lower index: no alternative
+    s_tie = np.array([[0.4, 0.2, 0.1, 0.2, 0.1]])
+    assert oracle.near_tie_alternatives(s_tie, 2) == {}
+    idx, _, margin = oracle.top_k_gates(s_tie, 2)
+    assert idx.tolist() == [[0, 1]] and margin[0] == 0.0
 
 
 def test_combine_outputs_closed_form():
