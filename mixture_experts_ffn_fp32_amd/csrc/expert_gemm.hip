@@ -355,10 +355,9 @@ __device__ __forceinline__ void load_frags(const uint8_t* __restrict__ rd, int k
 // ---------------------------------------------------------------- pipelined LDS-DMA kernel
 // Tiles of 256 rows x 256 B rows (GEMM1: 128 gate + 128 up rows of the same
 // columns; GEMM2: 256 output columns), W wavefronts in (W/2) x 2, each owning
-// 512/W rows x 128 columns (FM x 4 fragments of 32 x 32).  With W = 4 each
-// wavefront holds 256 float32 accumulators (in AGPRs) and every LDS fragment
-// feeds four MFMAs: a third less LDS read traffic than W = 8.  Operands reach LDS by
-// direct-to-LDS loads (global_load_lds_dwordx4: lane L of a wavefront writes
+// 512/W rows x 128 columns (FM x 4 fragments of 32 x 32; W = 8, two
+// wavefronts per SIMD).  Operands reach LDS by
+// direct-to-LDS loads (buffer_load_dwordx4 ... lds: lane L of a wavefront writes
 // 16 bytes at the wavefront's LDS address + 16 L), one 128-byte k-step per
 // row, in a two-slot ring: k-step s + 1 lands while k-step s is multiplied.
 // The LDS swizzle is applied on the global side (lane L fetches the chunk that
@@ -429,12 +428,7 @@ __device__ __forceinline__ void pipe_issue(const ExpertArgs& a, const Tile& ti,
 }
 
 // The k-groups of one k-step that also issue the other slot's loads.
-#ifndef MOE_DMA_GROUPS
-#define MOE_DMA_GROUPS 2
-#endif
-#ifndef MOE_SCHED_PATTERN
-#define MOE_SCHED_PATTERN 1
-#endif
+constexpr int kDmaGroups = 2;
 
 // Multiplies one k-step out of slot `rd` and issues the direct-to-LDS loads
 // of the other slot (base `db`, lane offsets `off`, into `wr`).  The
@@ -448,7 +442,7 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm,
                                          f32x16 (&acc)[FM][4], bool active,
                                          const uint8_t* db, const uint32_t (&off)[NI],
                                          uint8_t* __restrict__ wr, int nrec = 0x7fffffff) {
-  constexpr int FN = 4, KG = kPipeRB / 32, PARTS = MOE_DMA_GROUPS, PER = NI / PARTS;
+  constexpr int FN = 4, KG = kPipeRB / 32, PARTS = kDmaGroups, PER = NI / PARTS;
   static_assert(NI % PARTS == 0 && PARTS <= KG, "DMA parts");
   if (!active) {
 #pragma unroll
@@ -475,7 +469,6 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm,
                           ? mfma32(E{}, bfr[kg & 1][fn], af[kg & 1][fm], acc[fm][fn])
                           : mfma32(E{}, af[kg & 1][fm], bfr[kg & 1][fn], acc[fm][fn]);
   }
-#if MOE_SCHED_PATTERN
   // the layout: group 0's fragment reads first, then per k-group g its MFMAs,
   // each followed by one of group g + 1's reads and one of its loads
   __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
@@ -489,7 +482,6 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm,
       if (m < nd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   }
-#endif
 }
 
 // SiLU(g) * u with the hardware exp2 and reciprocal (a few float32 ulp).
@@ -519,12 +511,6 @@ __device__ __forceinline__ void pipe_store_bf16(const ExpertArgs& a, const Tile&
     if (MODE == 1 || wn == pass) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        if (FM == 4) {
-          // the accumulators stay in AGPRs up to here: copied to VGPRs one
-          // row fragment at a time, not all at the loop exit
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
-        }
         const int row = (wm * FM + fm) * 32 + lc;
         uint8_t* rowp = stage + row * (COLS * 2) + lh * 8;
         const int sw = row & 15;
@@ -695,11 +681,8 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
     const int nreal = Kc / kStep;
     const int nsteps = nreal + (nreal & 1);
     // A wavefront whose rows all lie past the expert's last slot skips its
-    // MFMAs when it shares a SIMD (W = 8); with one wavefront per SIMD (W = 4)
-    // skipping saves no time, and the branch would force the accumulators
-    // out of AGPRs, so every wavefront multiplies (the padded rows repeat
-    // the expert's last slot and are never stored).
-    const bool active = W == 4 || ti.m0 + wm * FM * 32 < ti.rows;
+    // MFMAs (the other wavefront on its SIMD gets the MFMA unit).
+    const bool active = ti.m0 + wm * FM * 32 < ti.rows;
     // The block's next tile, needed at the last k-step, is claimed at the end
     // of the first k-step: the wait for the counter's reply then coincides
     // with the wait for that k-step's loads (with only two k-steps it is
@@ -1008,24 +991,6 @@ bool small_m(const ExpertArgs& a) {
   return (long long)a.T * a.K < 64LL * (a.sel_N > 0 ? a.sel_N : a.N);
 }
 
-// MOE_GEMM_VARIANT=reg forces the register-staged kernel (read once; for tuning runs).
-bool force_reg() {
-  static int v = [] {
-    const char* e = getenv("MOE_GEMM_VARIANT");
-    return (e != nullptr && !strcmp(e, "reg")) ? 1 : 0;
-  }();
-  return v != 0;
-}
-
-// MOE_GEMM_VARIANT=pipe4 selects the four-wavefront pipelined kernel.
-int pipe_waves() {
-  static int v = [] {
-    const char* e = getenv("MOE_GEMM_VARIANT");
-    return (e != nullptr && !strcmp(e, "pipe4")) ? 4 : 8;
-  }();
-  return v;
-}
-
 // The pipelined kernel takes any shape the ABI admits (d and I multiples of
 // 64: whole 128-byte k-steps; an odd k-step count gets one zero-filled
 // k-step; partial last n-tiles are masked).
@@ -1039,17 +1004,16 @@ bool stream_long(int mode, const ExpertArgs& a) {
 }
 
 Shape shape1(const ExpertArgs& a, int es) {
-  if (small_m(a) && es == 2 && !force_reg())
-    return Shape{stream_long(1, a) ? 3 : 2, 0, 0, 0, 0};
+  if (small_m(a) && es == 2) return Shape{stream_long(1, a) ? 3 : 2, 0, 0, 0, 0};
   if (small_m(a)) return a.I % 128 == 0 ? Shape{0, 1, 4, 1, 2} : Shape{0, 2, 2, 1, 2};
-  if (!force_reg() && pipe_ok1(a, es)) return Shape{1, 4, 2, 2, 4};
+  if (pipe_ok1(a, es)) return Shape{1, 4, 2, 2, 4};
   return Shape{0, 2, 2, 2, 2};
 }
 Shape shape2(const ExpertArgs& a, int es) {
-  if (small_m(a) && es == 2 && !force_reg() && stream_long(2, a)) return Shape{3, 0, 0, 0, 0};
-  if (small_m(a) && es == 2 && !force_reg() && a.d % kStrBR == 0) return Shape{2, 0, 0, 0, 0};
+  if (small_m(a) && es == 2 && stream_long(2, a)) return Shape{3, 0, 0, 0, 0};
+  if (small_m(a) && es == 2 && a.d % kStrBR == 0) return Shape{2, 0, 0, 0, 0};
   if (small_m(a)) return a.d % 256 == 0 ? Shape{0, 1, 4, 1, 2} : Shape{0, 2, 2, 1, 1};
-  if (!force_reg() && pipe_ok2(a, es)) return Shape{1, 4, 2, 2, 4};
+  if (pipe_ok2(a, es)) return Shape{1, 4, 2, 2, 4};
   return a.d % 128 == 0 ? Shape{0, 2, 2, 2, 2} : Shape{0, 2, 2, 2, 1};
 }
 
@@ -1112,13 +1076,7 @@ hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
     if (s.kind == 2) return launch_stream<MODE>(a, st);
     if (s.kind == 3) return launch_stream_long(MODE, a, cu_count(), st);
   }
-  if (s.kind == 1) {
-    // float32 keeps eight wavefronts (its four-wavefront build spills)
-    if constexpr (std::is_same<E, ElemF32>::value)
-      return launch_pipe<E, MODE, 8>(a, st);
-    else
-      return pipe_waves() == 8 ? launch_pipe<E, MODE, 8>(a, st) : launch_pipe<E, MODE, 4>(a, st);
-  }
+  if (s.kind == 1) return launch_pipe<E, MODE, 8>(a, st);
   if (MODE == 1) {
     if (s.WM == 1) return launch_reg<E, 1, 4, 1, 2, 1>(a, st);
     if (s.FM == 1) return launch_reg<E, 2, 2, 1, 2, 1>(a, st);

@@ -10,9 +10,6 @@ namespace {
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n)&0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
 #define MOE_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14))
-#ifndef MOE_DMA_BUFFER
-#define MOE_DMA_BUFFER 1
-#endif
 
 // One direct-to-LDS load: 16 bytes per lane from `base` + `off` (base
 // wavefront-uniform) to LDS `wr` + 16 * lane.  It is issued as a buffer load
@@ -23,15 +20,10 @@ namespace {
 // `nrec` bounds the offsets (bytes): 0 makes the load return zeros.
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* __restrict__ wr,
                                       int nrec = 0x7fffffff) {
-#if MOE_DMA_BUFFER
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wr, 16, off,
                                            0, 0, 0);
-#else
-  __builtin_amdgcn_global_load_lds((const void*)(base + off),
-                                   (__attribute__((address_space(3))) void*)wr, 16, 0, 0);
-#endif
 }
 
 // Keeps a wavefront-uniform value in a scalar register.

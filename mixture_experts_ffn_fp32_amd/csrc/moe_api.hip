@@ -50,6 +50,21 @@ moe_status_t check_dim(const char* name, int x) {
   return MOE_OK;
 }
 
+// The MFMA GEMMs address the rows of an operand as 32-bit byte offsets from
+// one base inside a buffer resource whose range ends at 2^31 bytes: the
+// gathered token rows (u, and dh in the backward), the expert-sorted H
+// rows, the shared experts' H rows, one expert's weight block, and in the
+// backward the 256-row tiles of the transposed token copies.  Larger
+// operands are refused rather than read wrong.
+constexpr long long kMaxOperandBytes = 0x7fffffffLL - 4096;
+
+moe_status_t check_extent(const char* what, long long bytes) {
+  if (bytes > kMaxOperandBytes)
+    return fail(MOE_ERR_UNSUPPORTED, std::string(what) + " would span " +
+                                         std::to_string(bytes) + " bytes; the limit is 2^31");
+  return MOE_OK;
+}
+
 moe_status_t check_shapes(int T, int d, int I, int N, int K, int K_s, int dtype) {
   moe_status_t s;
   if ((s = check_dtype(dtype)) != MOE_OK) return s;
@@ -58,6 +73,11 @@ moe_status_t check_shapes(int T, int d, int I, int N, int K, int K_s, int dtype)
   if (K_s > 16) return fail(MOE_ERR_UNSUPPORTED, "K_s > 16 shared experts is not supported");
   if ((s = check_dim("d", d)) != MOE_OK) return s;
   if ((s = check_dim("I", I)) != MOE_OK) return s;
+  const long long es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  if ((s = check_extent("u [T][d]", (long long)T * d * es)) != MOE_OK) return s;
+  if ((s = check_extent("H_routed [T*K][I]", (long long)T * K * I * es)) != MOE_OK) return s;
+  if ((s = check_extent("H_shared [T][K_s*I]", (long long)T * K_s * I * es)) != MOE_OK) return s;
+  if ((s = check_extent("one expert's weights [3][I][d]", 3LL * I * d * es)) != MOE_OK) return s;
   return MOE_OK;
 }
 
@@ -572,11 +592,25 @@ BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype)
   return L;
 }
 
+// The backward's operands beyond the forward's: [da dc] rows (2I wide) and
+// 256-row tiles of the transposed token copies (pitch: every padded slot
+// column plus the shared experts' tokens).
+moe_status_t check_bwd_shapes(int T, int d, int I, int N, int K, int K_s, int dtype) {
+  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  if (s != MOE_OK) return s;
+  const long long es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  if ((s = check_extent("[da dc] [T*K][2I]", (long long)T * K * 2 * I * es)) != MOE_OK) return s;
+  const long long ldx = moe::bt_routed_cols(T, K, N) + moe::bt_pad64(T);
+  if ((s = check_extent("a 256-row tile of the transposed tokens", 256LL * ldx * 2)) != MOE_OK)
+    return s;
+  return MOE_OK;
+}
+
 }  // namespace
 
 moe_status_t moe_backward_workspace_size(int T, int d, int I, int N, int K, int K_s, int dtype,
                                          size_t* bytes) {
-  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  moe_status_t s = check_bwd_shapes(T, d, I, N, K, K_s, dtype);
   if (s != MOE_OK) return s;
   if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = T == 0 ? 0 : make_bwd_layout(T, d, I, N, K, K_s, dtype).total;
@@ -589,7 +623,7 @@ moe_status_t moe_layer_backward(const void* u, const void* E_gate, const void* W
                                 float* dE_gate, float* dgate_bias, float* dW_routed,
                                 float* dW_shared, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  moe_status_t s = check_bwd_shapes(T, d, I, N, K, K_s, dtype);
   if (s != MOE_OK) return s;
   if (T == 0) return ok();
   if ((s = check_ptr("u", u, true)) != MOE_OK) return s;

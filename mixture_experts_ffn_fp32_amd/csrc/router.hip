@@ -64,11 +64,9 @@ __device__ __forceinline__ int router_lds_offset(int r, int c) {
 
 // F: experts padded to 16F.  CH: 16-byte chunks of each row loaded per
 // k-step (long k-steps keep many loads in flight per wavefront: the kernel
-// is bound by the latency of reading u once).  TB: tokens per block; the
-// 4 wavefronts form 4 / WG groups of 16 tokens, the WG = 64 / TB wavefronts
-// of a group share its expert fragments (f % WG) and meet in LDS for the
-// softmax, which the group's first wavefront computes.
-template <class E, int F, int CH, int TB>
+// is bound by the latency of reading u once).  TB = 64 tokens per block,
+// wavefront w computing tokens 16w .. 16w + 15 against every expert.
+template <class E, int F, int CH>
 __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __restrict__ u,
                                                      const typename E::T* __restrict__ Eg,
                                                      const float* __restrict__ bias, int T, int d,
@@ -76,16 +74,16 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
                                                      float* __restrict__ gate,
                                                      float* __restrict__ scores) {
   using Tp = typename E::T;
+  constexpr int TB = 64;                // tokens per block
   constexpr int NP = 16 * F;            // experts, padded
   constexpr int ROWS = TB + NP;         // LDS rows per stage: tokens, then experts
-  constexpr int WG = 64 / TB;           // wavefronts per group of 16 tokens
   constexpr int RPP = 256 / CH;         // rows covered by one pass of the block
   constexpr int PASSES = (ROWS + RPP - 1) / RPP;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][ROWS * CH * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * TB;
-  const int tg = wave / WG, wr = wave % WG;  // token group, rank inside it
+  const int tg = wave;                  // the wavefront's group of 16 tokens
   constexpr int kStep = CH * E::kPerChunk;  // contraction elements per stage
   const int nsteps = d / kStep;
 
@@ -134,7 +132,6 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
       const u32x4 a = *(const u32x4*)(lds[buf] + router_lds_offset<CH>(tg * 16 + (lane & 15), ch));
 #pragma unroll
       for (int f = 0; f < F; ++f) {
-        if (WG > 1 && f % WG != wr) continue;
         const u32x4 b =
             *(const u32x4*)(lds[buf] + router_lds_offset<CH>(TB + f * 16 + (lane & 15), ch));
         acc[f] = mfma16(E{}, a, b, acc[f]);
@@ -146,21 +143,6 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
 
   // acc[f][r]: token row tg*16 + 4*(lane/16) + r, expert f*16 + lane%16.
   const int grp = lane >> 4, col = lane & 15;
-  if constexpr (WG > 1) {
-    // the group's fragments meet in LDS (the ring is free after the last barrier)
-    float* lg = (float*)&lds[0][0] + tg * 16 * NP;
-#pragma unroll
-    for (int f = 0; f < F; ++f)
-      if (f % WG == wr)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lg[(grp * 4 + r) * NP + f * 16 + col] = acc[f][r];
-    __syncthreads();
-    if (wr != 0) return;
-#pragma unroll
-    for (int f = 0; f < F; ++f)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[f][r] = lg[(grp * 4 + r) * NP + f * 16 + col];
-  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = t0 + tg * 16 + grp * 4 + r;
@@ -375,50 +357,30 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
   }
 }
 
-template <class E, int F, int TB>
-hipError_t launch_router_tb(const void* u, const void* Eg, const float* bias, int T, int d, int N,
-                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
-  using Tp = typename E::T;
-  const dim3 grid((T + TB - 1) / TB), block(256);
-  const Tp* up = (const Tp*)u;
-  const Tp* ep = (const Tp*)Eg;
-  // long k-steps (two stages of (TB + 16F) rows in LDS) where d allows
-  constexpr int CH = F <= 4 ? 32 : F == 8 ? 16 : 8;
-  if ((size_t)d * sizeof(Tp) % (CH * 16) == 0)
-    router_kernel<E, F, CH, TB><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  else
-    router_kernel<E, F, 8, TB><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  return hipGetLastError();
-}
-
-// Tokens per block: 64 (measured fastest at both the decode and the prefill
-// sizes: each block is bound by the latency of its k-steps, not by the
-// number of blocks).  MOE_ROUTER_TB=16 or 32 selects the expert-split
-// layouts (tuning runs; results are identical).
-int router_tb(int T) {
-  (void)T;
-  static const int v = [] {
-    const char* e = getenv("MOE_ROUTER_TB");
-    return e == nullptr ? 64 : atoi(e) == 16 ? 16 : atoi(e) == 32 ? 32 : 64;
-  }();
-  return v;
-}
-
-// Batches of at most kSmallRouterMaxT tokens take the one-block-per-token
-// kernel unless MOE_ROUTER_SMALL=0.
-bool router_small() {
-  const char* e = getenv("MOE_ROUTER_SMALL");
-  return !(e != nullptr && e[0] == '0');
-}
-
+// One block per 64 tokens (measured fastest against 16- and 32-token blocks
+// that split the experts over wavefronts: each block is bound by the latency
+// of its k-steps, not by the number of blocks).
 template <class E, int F>
 hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int T, int d, int N,
                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
-  switch (router_tb(T)) {
-    case 16: return launch_router_tb<E, F, 16>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
-    case 32: return launch_router_tb<E, F, 32>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
-    default: return launch_router_tb<E, F, 64>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
-  }
+  using Tp = typename E::T;
+  const dim3 grid((T + 63) / 64), block(256);
+  const Tp* up = (const Tp*)u;
+  const Tp* ep = (const Tp*)Eg;
+  // long k-steps (two stages of (64 + 16F) rows in LDS) where d allows
+  constexpr int CH = F <= 4 ? 32 : F == 8 ? 16 : 8;
+  if ((size_t)d * sizeof(Tp) % (CH * 16) == 0)
+    router_kernel<E, F, CH><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
+  else
+    router_kernel<E, F, 8><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
+  return hipGetLastError();
+}
+
+// Batches of at most kSmallRouterMaxT tokens take the one-block-per-token
+// kernel unless MOE_ROUTER_SMALL=0 (read on every call).
+bool router_small() {
+  const char* e = getenv("MOE_ROUTER_SMALL");
+  return !(e != nullptr && e[0] == '0');
 }
 
 template <class E>

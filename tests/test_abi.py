@@ -67,6 +67,32 @@ def test_workspace_size_validation(lib):
         assert lib.moe_last_error().decode()
 
 
+def test_operands_past_2gib_are_refused(lib):
+    """Operand rows are addressed as 32-bit byte offsets inside a 2 GiB buffer range:
+    shapes whose u, H_routed, H_shared or one expert's weights would span more are
+    refused with MOE_ERR_UNSUPPORTED instead of computing a wrong h."""
+    # T, d, I, N, K, K_s, dtype
+    cases = [
+        (32768, 2048, 1536, 64, 12, 2, 0),     # f32 H_routed: 32768*12*1536*4 = 2.4 GB
+        (65536, 16384, 64, 8, 1, 0, 1),        # bf16 u: 65536*16384*2 = 2 GiB
+        (65536, 1024, 2048, 8, 1, 16, 1),      # bf16 H_shared: 65536*16*2048*2 = 4 GiB
+        (1, 16384, 32768, 8, 1, 0, 1),         # one expert block 3*I*d*2 = 3 GiB
+    ]
+    for shape in cases:
+        st, _ = _ws(lib, *shape)
+        assert st == UNSUPPORTED, (shape, st)
+        assert "2^31" in lib.moe_last_error().decode()
+    # the largest workload shape stays well inside the limit
+    assert _ws(lib, 16384, 4096, 1536, 128, 12, 4, 1)[0] == OK
+    out = ctypes.c_size_t(0)
+    assert lib.moe_backward_workspace_size(16384, 4096, 1536, 128, 12, 4, 1,
+                                           ctypes.byref(out)) == OK
+    # the backward's [da dc] rows: 2 * H_routed
+    assert lib.moe_backward_workspace_size(20000, 1024, 4096, 64, 8, 0, 1,
+                                           ctypes.byref(out)) == UNSUPPORTED
+    assert lib.moe_workspace_size(20000, 1024, 4096, 64, 8, 0, 1, ctypes.byref(out)) == OK
+
+
 def test_workspace_size_grows_with_tokens(lib):
     sizes = [_ws(lib, T, 2048, 1408, 64, 6, 2, 1)[1] for T in (1, 64, 65, 1000, 8192)]
     assert sizes == sorted(sizes) and len(set(sizes)) == len(sizes)

@@ -2,10 +2,12 @@
 145B-skewed-shaped bf16 layers), in the launch configuration the benchmark times.
 
 Routing is checked on every token; dispatch on every pair (integer exact); the
-expert stage on the hottest, the coldest and two random experts; h on every
-token where the oracle finishes in seconds, else on a sample that holds the
-first and last tokens, every near-tie token, tokens of the hottest and coldest
-experts and random tokens.
+expert stage on every slot of every expert (H and Y, so every m-tile including
+each expert's ragged tail tile) and on every token row of the shared experts,
+except at the 145B shape, where it covers every slot of the hottest, the
+coldest and two random experts (plus every shared row); h on every token,
+except at the 145B shape: 2048 tokens holding the first and last tokens, every
+near-tie token, tokens of the hottest and coldest experts and random tokens.
 """
 import numpy as np
 import pytest
@@ -20,8 +22,10 @@ pytestmark = pytest.mark.gpu
 mx = pytest.importorskip("mixture_experts_ffn_fp32_amd")
 
 # tokens whose h is recomputed by the oracle (None = all)
-SAMPLE = {"tiny_fp32": None, "moe16b_decode_bf16": None, "moe2b_bf16": 384,
-          "moe16b_prefill_bf16": 192, "moe145b_skewed_bf16": 96}
+SAMPLE = {"tiny_fp32": None, "moe16b_decode_bf16": None, "moe2b_bf16": None,
+          "moe16b_prefill_bf16": None, "moe145b_skewed_bf16": 2048}
+# experts whose every slot the expert-stage test checks (None = all)
+STAGE_EXPERTS = {"moe145b_skewed_bf16": 4}
 
 
 @pytest.fixture(scope="module", params=list(moe_inputs.WORKLOADS))
@@ -48,8 +52,8 @@ def _sample(up, s, n):
     rng = np.random.default_rng(w.seed)
     pick = {0, w.T - 1}
     pick |= set(np.nonzero(margin <= 1e-6)[0].tolist())
-    pick |= set(np.nonzero((idx == cold).any(axis=1))[0][:8].tolist())
-    pick |= set(np.nonzero((idx == hot).any(axis=1))[0][:8].tolist())
+    pick |= set(np.nonzero((idx == cold).any(axis=1))[0].tolist())     # all of the coldest
+    pick |= set(np.nonzero((idx == hot).any(axis=1))[0][:64].tolist())
     while len(pick) < n:
         pick.add(int(rng.integers(w.T)))
     return np.array(sorted(pick))
@@ -92,35 +96,40 @@ def test_expert_stage_selected_experts(wl):
                                  torch.from_numpy(g_ref.astype(np.float32)).cuda())
     torch.cuda.synchronize()
     nz = np.nonzero(c_ref)[0]
-    rng = np.random.default_rng(3)
-    experts = sorted({int(np.argmax(c_ref)), int(nz[np.argmin(c_ref[nz])]),
-                      *rng.choice(nz, size=min(2, nz.size), replace=False).tolist()})
+    n_pick = STAGE_EXPERTS.get(w.name)
+    if n_pick is None:
+        experts = nz.tolist()
+    else:
+        rng = np.random.default_rng(3)
+        experts = sorted({int(np.argmax(c_ref)), int(nz[np.argmin(c_ref[nz])]),
+                          *rng.choice(nz, size=min(n_pick - 2, nz.size), replace=False).tolist()})
     tol = tol_for(w)
-    # at most 256 rows per expert keep the oracle's share of the time bounded
-    for e in experts:
-        lo, hi = int(o_ref[e]), int(o_ref[e + 1])
-        hi = min(hi, lo + 256)
-        pairs = sp_ref[lo:hi]
-        # H and Y of these rows from the oracle's own slot activations
-        o_one = np.zeros(w.N + 1, dtype=np.int64)
-        o_one[e + 1:] = hi - lo
-        sp_one = np.zeros(hi - lo, dtype=np.int64)
-        sp_one[:] = pairs
-        acts, _ = oracle.expert_slot_activations(up.inp.u_f32(), up.routed, up.shared, idx_ref,
-                                                 g_ref, sp_one, o_one, w.K, 0, experts=[e])
+    u32 = up.inp.u_f32()
+    for e in experts:    # every slot of the expert: all its m-tiles, the ragged last one too
+        acts, _ = oracle.expert_slot_activations(u32, up.routed, up.shared, idx_ref, g_ref,
+                                                 sp_ref, o_ref, w.K, 0, experts=[e])
         H_ref, Y_ref = acts[e]
+        lo, hi = int(o_ref[e]), int(o_ref[e + 1])
         Hg = device_f32(H[lo:hi])
-        Yg = device_f32(Y[torch.from_numpy(pairs).cuda()])
+        Yg = device_f32(Y[torch.from_numpy(sp_ref[lo:hi]).cuda()])
         assert np.abs(Hg - H_ref).max() <= tol * np.abs(H_ref).max(), f"H of expert {e}"
         assert np.abs(Yg - Y_ref).max() <= tol * np.abs(Y_ref).max(), f"Y of expert {e}"
+    say(f"{w.name}: H and Y of {len(experts)} experts, {int(c_ref[experts].sum())} slots")
     if w.K_s:
-        rows = np.arange(min(w.T, 128))
-        _, sh = oracle.expert_slot_activations(up.inp.u_f32()[rows], up.routed, up.shared,
-                                               idx_ref[rows], g_ref[rows], sp_ref[:0],
-                                               np.zeros(1, dtype=np.int64), w.K, w.K_s, experts=[])
-        Ys_ref = sum(sh[j][1] for j in range(w.K_s))
-        Ysg = device_f32(Ys[:len(rows)])
-        assert np.abs(Ysg - Ys_ref).max() <= tol * np.abs(Ys_ref).max(), "Y_shared"
+        Hs_g = device_f32(Hs)
+        Ys_g = device_f32(Ys)
+        for r0 in range(0, w.T, 4096):     # every token row, in row blocks
+            rows = np.arange(r0, min(w.T, r0 + 4096))
+            _, sh = oracle.expert_slot_activations(u32[rows], up.routed, up.shared,
+                                                   idx_ref[rows], g_ref[rows], sp_ref[:0],
+                                                   np.zeros(1, dtype=np.int64), w.K, w.K_s,
+                                                   experts=[])
+            for j in range(w.K_s):
+                H_ref = sh[j][0]
+                Hg = Hs_g[rows][:, j * w.I:(j + 1) * w.I]
+                assert np.abs(Hg - H_ref).max() <= tol * np.abs(H_ref).max(), f"H_shared {j}"
+            Ys_ref = sum(sh[j][1] for j in range(w.K_s))
+            assert np.abs(Ys_g[rows] - Ys_ref).max() <= tol * np.abs(Ys_ref).max(), "Y_shared"
 
 
 def test_layer_forward_sampled(wl):
@@ -168,6 +177,11 @@ def test_balance_statistics(wl):
     np.testing.assert_allclose(res["P"].cpu().numpy(), ref["P"], rtol=1e-5, atol=1e-7)
     assert abs(float(res["L_ExpBal"]) - ref["L_ExpBal"]) <= 1e-4 * ref["L_ExpBal"] + 1e-3 * n_near
     np.testing.assert_allclose(res["P_dev"].cpu().numpy(), ref["P_dev"], rtol=1e-5, atol=1e-7)
+    # f'_g: the mean of f over the group's N / D experts (a near tie moves one f by f_step)
+    assert np.abs(res["f_dev"].cpu().numpy() - ref["f_dev"]).max() <= \
+        f_step * n_near + 2.0 ** -22 * ref["f_dev"].max()
+    assert abs(float(res["L_DevBal"]) - ref["L_DevBal"]) <= \
+        1e-4 * ref["L_DevBal"] + 2 * 0.05 * f_step * n_near
     assert abs(float(res["f"].double().sum()) - w.N) <= 1e-5 * w.N
     assert abs(float(res["P"].double().sum()) - 1.0) <= 1e-5
     if w.zipf_s is not None:   # the skew shows: the hottest expert far above f = 1
