@@ -56,20 +56,21 @@ def test_route_small_batch_kernels_agree(name, monkeypatch):
 
 def _tie_inputs(T, d, N, K, pattern, dtype, with_bias, seed):
     """Router inputs whose scores have planted EXACT ties: every token ranks the experts in
-    the same order (expert perm[r] at rank r, logit levels one unit apart), and the experts
-    of one tie group have bit-identical centroid rows (and biases), so their logits are
-    equal on both sides whatever the token.  `pattern` lists the rank groups that tie."""
+    the same order (expert perm[r] at rank r, logits about one unit apart, the top one near
+    0), and the experts of one tie group have bit-identical centroid rows (and biases), so
+    their logits are equal on both sides whatever the token.  `pattern` lists the rank
+    groups that tie."""
     rng = np.random.default_rng(seed)
     perm = rng.permutation(N)
     level = np.zeros(N, dtype=np.float32)
     noise = rng.standard_normal((N, d - 1)).astype(np.float32) * 0.01
-    bias = rng.standard_normal(N).astype(np.float32) * 0.25
+    bias = rng.standard_normal(N).astype(np.float32) * 0.05
     lead = {}
     for grp in pattern:
         for r in grp[1:]:
             lead[r] = grp[0]
     for r in range(N):
-        level[perm[r]] = float(N - lead.get(r, r))
+        level[perm[r]] = -0.5 * lead.get(r, r)
         noise[perm[r]] = noise[perm[lead.get(r, r)]]
         bias[perm[r]] = bias[perm[lead.get(r, r)]]
     E = np.concatenate([level[:, None], noise], axis=1)
@@ -123,8 +124,10 @@ def test_route_exact_ties_go_to_lower_index(case, dtype, router, monkeypatch):
         for grp in tie_sets:                 # equal on the GPU too
             assert np.all(sc[:, grp] == sc[:, grp[:1]])
         np.testing.assert_array_equal(ig, idx_ref)   # set and order, bit-exact
-        np.testing.assert_allclose(gate.cpu().numpy(), g_ref, rtol=1e-5)
-        check_routing(ig, gate.cpu().numpy(), s_ref, K)
+        # logits of a few units here (float32 products and sums of inputs this large move
+        # a score by ~|z| 2^-24 sqrt(d) relative), so the gates get a wider band
+        np.testing.assert_allclose(gate.cpu().numpy(), g_ref, rtol=1e-4)
+        check_routing(ig, gate.cpu().numpy(), s_ref, K, gate_rtol=1e-4)
 
 
 def test_dispatch(small):
