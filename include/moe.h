@@ -87,6 +87,29 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
                                int I, int dtype, const float* gate_bias, void* h,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- allocation-free forward ----
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels and results as moe_layer_forward (the same
+ * bits for the same inputs), with the workspace taken from a static device
+ * array of MOE_STATIC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends (its address is looked up on the first call
+ * made with that device current).  No hipMalloc, hipFree, stream, event or
+ * other allocating call is made; timing events and the MOE_SHARED_SIDE side
+ * stream are not used.
+ * Limits: shapes whose moe_workspace_size() exceeds MOE_STATIC_SCRATCH_BYTES
+ * are refused with MOE_ERR_WORKSPACE (at d = 2048, I = 1408, 64 routed
+ * experts, top-6 and 2 shared experts: up to about 1300 tokens).
+ * Every call on a device shares that device's one array: calls that overlap
+ * on one device (two streams, or two host threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the array needs
+ * to start at zero (each call writes every region before reading it). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_layer_forward_static(const void* u, const void* E_gate, const void* W_routed,
+                                      const void* W_shared, int N, int K, int K_s, int T, int d,
+                                      int I, int dtype, const float* gate_bias, void* h,
+                                      void* stream);
+
 /* ---- stage entry points: the kernels moe_layer_forward launches, one stage
  * at a time, for callers that want the intermediate results. ---- */
 

@@ -169,11 +169,13 @@ struct Timing {
 Timing g_timing;
 
 // Records an event pair around one stage when timing is on.
+// Calls that must not allocate pass record = false (event creation allocates).
 struct StageScope {
   int stage;
   hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
-  StageScope(int s, hipStream_t stream) : stage(s), st(stream) {
+  StageScope(int s, hipStream_t stream, bool record = true) : stage(s), st(stream) {
+    if (!record) return;
     std::lock_guard<std::mutex> g(g_timing.mu);
     if (!g_timing.on || !((g_timing.mask >> s) & 1u)) return;
     a = g_timing.get();
@@ -234,29 +236,29 @@ hipError_t side_of_device(Side** out) {
 moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* rank,
                           int32_t* tile_counts, int32_t* tile_base, hipStream_t st,
-                          const moe::TileTableOut* tables = nullptr) {
+                          const moe::TileTableOut* tables = nullptr, bool rec = true) {
   hipError_t e;
   const moe::TileTableOut tt = tables != nullptr ? *tables : moe::TileTableOut{};
   if (T <= moe::kRankTile) {  // one tile: ranks, scan and scatter in one launch
-    StageScope sc(1, st);
+    StageScope sc(1, st, rec);
     if ((e = moe::launch_dispatch_small(idx, T, N, K, counts, offsets, sorted_pair, tt, st)) !=
         hipSuccess)
       return hip_fail(e, "dispatch launch");
     return MOE_OK;
   }
   {
-    StageScope sc(1, st);
+    StageScope sc(1, st, rec);
     if ((e = moe::launch_tile_rank(idx, T, N, K, tile_counts, rank, st)) != hipSuccess)
       return hip_fail(e, "tile rank launch");
   }
   {
-    StageScope sc(2, st);
+    StageScope sc(2, st, rec);
     if ((e = moe::launch_dispatch_scan(tile_counts, rank_tiles(T), N, counts, offsets, tile_base,
                                        tt, st)) != hipSuccess)
       return hip_fail(e, "dispatch scan launch");
   }
   {
-    StageScope sc(3, st);
+    StageScope sc(3, st, rec);
     if ((e = moe::launch_scatter(idx, rank, tile_base, T, N, K, sorted_pair, st)) != hipSuccess)
       return hip_fail(e, "scatter launch");
   }
@@ -265,42 +267,28 @@ moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* coun
 
 // tables_ready: the dispatch launch has already written the tile tables.
 moe_status_t run_experts(int dtype, const moe::ExpertArgs& a, hipStream_t st,
-                         bool tables_ready = false) {
+                         bool tables_ready = false, bool rec = true) {
   hipError_t e;
   {
-    StageScope sc(4, st);
+    StageScope sc(4, st, rec);
     if (!tables_ready && (e = moe::launch_tile_table(dtype, a, st)) != hipSuccess)
       return hip_fail(e, "tile table launch");
     if ((e = moe::launch_gemm1(dtype, a, st)) != hipSuccess)
       return hip_fail(e, "expert GEMM1 launch");
   }
   {
-    StageScope sc(5, st);
+    StageScope sc(5, st, rec);
     if ((e = moe::launch_gemm2(dtype, a, st)) != hipSuccess)
       return hip_fail(e, "expert GEMM2 launch");
   }
   return MOE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* moe_last_error(void) { return g_err.c_str(); }
-
-moe_status_t moe_workspace_size(int T, int d, int I, int N, int K, int K_s, int dtype,
-                                size_t* bytes) {
-  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
-  if (s != MOE_OK) return s;
-  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = T == 0 ? 0 : make_layout(T, d, I, N, K, K_s, dtype).total;
-  return ok();
-}
-
-moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_routed,
-                               const void* W_shared, int N, int K, int K_s, int T, int d, int I,
-                               int dtype, const float* gate_bias, void* h, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+// ---------------------------------------------------------------- the forward
+// Argument checks of the layer forward that do not involve the workspace.
+moe_status_t check_forward(const void* u, const void* E_gate, const void* W_routed,
+                           const void* W_shared, int N, int K, int K_s, int T, int d, int I,
+                           int dtype, const float* gate_bias, void* h) {
   moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
   if (s != MOE_OK) return s;
   if (T == 0) return ok();
@@ -310,16 +298,20 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
   if ((s = check_ptr("W_shared", W_shared, K_s > 0)) != MOE_OK) return s;
   if ((s = check_ptr("gate_bias", gate_bias, false)) != MOE_OK) return s;
   if ((s = check_ptr("h", h, true)) != MOE_OK) return s;
-  if ((s = check_ptr("workspace", workspace, true)) != MOE_OK) return s;
-  const size_t es = elem_size(dtype), act = (size_t)T * d * es;
+  const size_t act = (size_t)T * d * elem_size(dtype);
   if (overlap(h, act, u, act)) return fail(MOE_ERR_INVALID_ARG, "h overlaps u");
-  const Layout L = make_layout(T, d, I, N, K, K_s, dtype);
-  if (workspace_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size()");
-  if (overlap(h, act, workspace, L.total)) return fail(MOE_ERR_INVALID_ARG, "h overlaps workspace");
+  return MOE_OK;
+}
 
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
+// The launch sequence of the layer forward on workspace `ws` (layout L).
+// rec: record timing events when timing is on and allow the side stream
+// (both create HIP objects on first use; the allocation-free entry point
+// passes false).
+moe_status_t forward_enqueue(const void* u, const void* E_gate, const void* W_routed,
+                             const void* W_shared, int N, int K, int K_s, int T, int d, int I,
+                             int dtype, const float* gate_bias, void* h, char* ws,
+                             const Layout& L, hipStream_t st, bool rec) {
+  moe_status_t s;
   int32_t* idx = (int32_t*)(ws + L.idx);
   float* gate = (float*)(ws + L.gate);
   hipError_t e;
@@ -348,7 +340,7 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
   // decode-sized batches with MOE_SHARED_SIDE=1: the shared experts on the
   // side stream, the routed ones (a K_s = 0 view of the same buffers) after
   // the dispatch
-  const bool side = K_s > 0 && T <= kSideMaxT && side_enabled();
+  const bool side = rec && K_s > 0 && T <= kSideMaxT && side_enabled();
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
   Side* sd = nullptr;
   moe::ExpertArgs ar = a;
@@ -371,7 +363,7 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
     ar.K_s = 0;
   }
   {
-    StageScope sc(0, st);
+    StageScope sc(0, st, rec);
     if ((e = moe::launch_router(dtype, u, E_gate, gate_bias, T, d, N, K, idx, gate, nullptr, st)) !=
         hipSuccess)
       return hip_fail(e, "router launch");
@@ -379,18 +371,99 @@ moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_
   const moe::TileTableOut tables = moe::expert_tile_tables(dtype, ar);
   if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
                         (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
-                        (int32_t*)(ws + L.tile_base), st, &tables)) != MOE_OK)
+                        (int32_t*)(ws + L.tile_base), st, &tables, rec)) != MOE_OK)
     return s;
-  if ((s = run_experts(dtype, ar, st, true)) != MOE_OK) return s;
+  if ((s = run_experts(dtype, ar, st, true, rec)) != MOE_OK) return s;
   if (side && (e = hipStreamWaitEvent(st, sd->join, 0)) != hipSuccess)
     return hip_fail(e, "shared-expert join");
   if (side) side_lock.unlock();
   {
-    StageScope sc(6, st);
+    StageScope sc(6, st, rec);
     if ((e = moe::launch_combine(dtype, u, a.Y, a.Y_shared, T, d, K, K_s, h, st)) != hipSuccess)
       return hip_fail(e, "combine launch");
   }
   return ok();
+}
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of moe_layer_forward_static: a device array of the library's
+// own (each device holds its copy until the process ends).  Host code never
+// uses its name as an address: its device address is looked up once per
+// device and kept.
+constexpr size_t kScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[64] = {nullptr};
+
+// The scratch array's address on the current device (looked up on the first
+// call made with that device current).
+hipError_t scratch_of_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status_t moe_workspace_size(int T, int d, int I, int N, int K, int K_s, int dtype,
+                                size_t* bytes) {
+  moe_status_t s = check_shapes(T, d, I, N, K, K_s, dtype);
+  if (s != MOE_OK) return s;
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = T == 0 ? 0 : make_layout(T, d, I, N, K, K_s, dtype).total;
+  return ok();
+}
+
+moe_status_t moe_layer_forward(const void* u, const void* E_gate, const void* W_routed,
+                               const void* W_shared, int N, int K, int K_s, int T, int d, int I,
+                               int dtype, const float* gate_bias, void* h, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  moe_status_t s = check_forward(u, E_gate, W_routed, W_shared, N, K, K_s, T, d, I, dtype,
+                                 gate_bias, h);
+  if (s != MOE_OK || T == 0) return s;
+  if ((s = check_ptr("workspace", workspace, true)) != MOE_OK) return s;
+  const Layout L = make_layout(T, d, I, N, K, K_s, dtype);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size()");
+  const size_t act = (size_t)T * d * elem_size(dtype);
+  if (overlap(h, act, workspace, L.total)) return fail(MOE_ERR_INVALID_ARG, "h overlaps workspace");
+  return forward_enqueue(u, E_gate, W_routed, W_shared, N, K, K_s, T, d, I, dtype, gate_bias, h,
+                         (char*)workspace, L, (hipStream_t)stream, true);
+}
+
+moe_status_t moe_layer_forward_static(const void* u, const void* E_gate, const void* W_routed,
+                                      const void* W_shared, int N, int K, int K_s, int T, int d,
+                                      int I, int dtype, const float* gate_bias, void* h,
+                                      void* stream) {
+  moe_status_t s = check_forward(u, E_gate, W_routed, W_shared, N, K, K_s, T, d, I, dtype,
+                                 gate_bias, h);
+  if (s != MOE_OK || T == 0) return s;
+  const Layout L = make_layout(T, d, I, N, K, K_s, dtype);
+  if (L.total > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "these shapes need " + std::to_string(L.total) +
+                                       " bytes of workspace; the static scratch holds " +
+                                       std::to_string(kScratchBytes) +
+                                       " (use moe_layer_forward with a workspace)");
+  char* ws = nullptr;
+  hipError_t e = scratch_of_device(&ws);
+  if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  return forward_enqueue(u, E_gate, W_routed, W_shared, N, K, K_s, T, d, I, dtype, gate_bias, h,
+                         ws, L, (hipStream_t)stream, false);
 }
 
 moe_status_t moe_route(const void* u, const void* E_gate, const float* gate_bias, int T, int d,

@@ -20,7 +20,8 @@ STAGE_NAMES = ("router", "tile_rank", "dispatch_scan", "scatter", "expert_gemm1_
                "expert_gemm2_down", "combine")
 _DTYPES = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}
 
-EXPORTED = ("moe_last_error", "moe_workspace_size", "moe_layer_forward", "moe_route",
+EXPORTED = ("moe_last_error", "moe_workspace_size", "moe_layer_forward",
+            "moe_layer_forward_static", "moe_route",
             "moe_dispatch_workspace_size", "moe_dispatch", "moe_expert_ffn_workspace_size",
             "moe_expert_ffn", "moe_combine", "moe_balance_workspace_size", "moe_balance_stats",
             "moe_backward_workspace_size", "moe_layer_backward", "moe_timing_enable",
@@ -52,6 +53,7 @@ def load_library(path: str = LIB_PATH):
     sigs = {
         "moe_workspace_size": [i, i, i, i, i, i, i, szp],
         "moe_layer_forward": [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, sz, vp],
+        "moe_layer_forward_static": [vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp],
         "moe_route": [vp, vp, f, i, i, i, i, i, vp, vp, vp, vp],
         "moe_dispatch_workspace_size": [i, i, i, szp],
         "moe_dispatch": [vp, i, i, i, vp, vp, vp, vp, sz, vp],
@@ -139,6 +141,24 @@ def layer_forward(u, E_gate, W_routed, W_shared, N: int, K: int, K_s: int, gate_
     _check(L.moe_layer_forward(_p(u), _p(E_gate), _p(W_routed), _p(W_shared), N, K, K_s, T, d, I,
                                dt, _p(gate_bias), _p(h), _p(workspace),
                                workspace.numel() * workspace.element_size(), _stream()))
+    return h
+
+
+def layer_forward_static(u, E_gate, W_routed, W_shared, N: int, K: int, K_s: int,
+                         gate_bias=None, out=None):
+    """The layer forward with the library's static device scratch as its workspace (no
+    device allocation inside the call; `out` may be given so that none is made here
+    either).  Shapes needing more than MOE_STATIC_SCRATCH_BYTES raise MoEError."""
+    L = load_library()
+    T, d = u.shape
+    dt = _dtype_code(u)
+    _dev(u, E_gate, W_routed, W_shared, dtype=u.dtype)
+    _dev(gate_bias, dtype=torch.float32)
+    I = _infer_I(W_routed, N, d)
+    h = torch.empty_like(u) if out is None else out
+    _dev(h, dtype=u.dtype)
+    _check(L.moe_layer_forward_static(_p(u), _p(E_gate), _p(W_routed), _p(W_shared), N, K, K_s,
+                                      T, d, I, dt, _p(gate_bias), _p(h), _stream()))
     return h
 
 
