@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--backward-only", action="store_true",
                     help="only the layer backward of the workload (for profiling runs)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--other-workloads", default="moe2b_bf16:4096,moe145b_skewed_bf16:2048",
+                    help="comma-separated NAME:CPU_TOKENS of further workloads timed beside the "
+                         "main one (CPU_TOKENS: the oracle's token sample); empty for none")
     ap.add_argument("--sweep", action="store_true",
                     help="granularity sweep instead of the benchmark line: the same layer "
                          "cut into m in {1,2,4,8} times finer experts, K_s in {0,1} shared, at "
@@ -49,7 +52,10 @@ def parse():
     ap.add_argument("--profile-mode", action="store_true",
                     help="for hardware-counter runs: a 1 GiB device copy (calibration) and two "
                          "layer forwards of the workload, nothing else")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.other_workloads = [(n, int(c)) for n, c in
+                            (x.split(":") for x in args.other_workloads.split(",") if x)]
+    return args
 
 
 def profile_mode(args):
@@ -94,9 +100,11 @@ def upload(inp, device):
 
 
 def time_layer(mx, t, w, steps, warmup, stage_timing):
-    """Warm up, then time exactly `steps` forwards between two synchronisations.
+    """Warm up, then time exactly `steps` forwards between two synchronisations, with an
+    event between consecutive steps (per-step times for the median and percentiles).
     stage_timing: False, True (an event pair around every stage) or a list of stage
-    names (event pairs around those stages only)."""
+    names (event pairs around those stages only).
+    Returns (total ms, [ms of each step], {stage: (ms, launches)})."""
     import torch
 
     I = t["Wr"].numel() // (3 * w.N * w.d)
@@ -110,16 +118,50 @@ def time_layer(mx, t, w, steps, warmup, stage_timing):
     mx.timing_read()                       # drop anything recorded before
     mx.timing_enable(bool(stage_timing),
                      None if isinstance(stage_timing, bool) else list(stage_timing))
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         mx.layer_forward(*args, out=h, workspace=ws)
-    stop.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     mx.timing_enable(False)
     stages = mx.timing_read()
-    return start.elapsed_time(stop), stages
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]), per_step, stages
+
+
+def step_stats(per_step):
+    """Median, 10th and 90th percentile of the per-step times (ms)."""
+    import numpy as np
+
+    q = np.percentile(np.asarray(per_step), [50, 10, 90])
+    return {"median": round(float(q[0]), 4), "p10": round(float(q[1]), 4),
+            "p90": round(float(q[2]), 4)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def gemm_rooflines(w, stages, peak):
+    """TFLOP/s and fraction of peak of both expert GEMMs from the per-stage event pairs."""
+    out = {}
+    for key, per_pair in (("expert_gemm1_swiglu", 4.0), ("expert_gemm2_down", 2.0)):
+        ms, n = stages[key]
+        if not n:
+            continue
+        fl = per_pair * w.d * w.I * w.T * (w.K + w.K_s)
+        tf = fl / (ms / n / 1e3) / 1e12
+        out[key] = {"launch_ms": round(ms / n, 4), "tflops": round(tf, 2),
+                    "frac": round(tf / peak, 4)}
+    return out
 
 
 def time_backward(mx, t, w, steps, warmup):
@@ -161,7 +203,8 @@ def experts_hit(mx, t, w):
 
 
 def cpu_baseline(inp, n_tokens):
-    """The float64 oracle, as it stands, on the first n_tokens tokens of the workload."""
+    """The float64 oracle, as it stands, on the first n_tokens tokens of the workload
+    (the router over those tokens, each selected expert over its tokens among them)."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
@@ -178,7 +221,8 @@ def cpu_baseline(inp, n_tokens):
                               inp.gate_bias(), tokens)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(len(tokens) / dt, 1), "unit": "tokens/s", "cores": threads,
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"first {len(tokens)} of {w.T} tokens of {w.name} (router over the sample, "
                       f"all experts' weights decoded), {dt:.2f} s wall"}
 
@@ -207,14 +251,15 @@ def sweep(args):
              "Ws": (torch.randn(w.K_s * 3 * w.I * w.d, generator=g, device=dev, dtype=bf) * w.sigma
                     if w.K_s else None),
              "bias": None}
-        ms, _ = time_layer(mx, t, w, args.steps, args.warmup, False)
-        _, stages = time_layer(mx, t, w, args.steps, 1, True)
+        ms, per_step, _ = time_layer(mx, t, w, args.steps, args.warmup, False)
+        _, _, stages = time_layer(mx, t, w, args.steps, 1, True)
         step = ms / args.steps / 1e3
         tflops = w.flops_per_token() * w.T / step / 1e12
         print(json.dumps({
             "sweep": w.name, "m": m, "shared_experts": ks, "routed_experts": w.N, "top_k": w.K,
             "intermediate": w.I, "T": w.T, "d": w.d, "dtype": w.dtype,
-            "ms_per_step": round(step * 1e3, 4), "tokens_per_s": round(w.T / step, 1),
+            "ms_per_step": round(step * 1e3, 4), "step_ms": step_stats(per_step),
+            "tokens_per_s": round(w.T / step, 1),
             "layer_tflops": round(tflops, 2), "layer_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items()}}), flush=True)
         del t
@@ -252,6 +297,35 @@ def traffic_record(kernel_src: str, key: str):
     return rec.get("bytes_per_launch")
 
 
+def other_workload(mx, name, steps, warmup, cpu_tokens):
+    """One more prefill-sized workload, reported beside the main line: tokens/s, the step
+    time's median and percentiles, the layer's and each GEMM's fraction of bf16 MFMA
+    peak, the stage times, and the oracle on a token sample (None: no CPU baseline)."""
+    import torch
+
+    import moe_inputs
+
+    inp = moe_inputs.make(name)
+    w = inp.w
+    t = upload(inp, torch.device("cuda:0"))
+    ms, per_step, _ = time_layer(mx, t, w, steps, warmup, False)
+    _, _, stages = time_layer(mx, t, w, steps, 1, True)
+    del t
+    torch.cuda.empty_cache()
+    step = ms / steps
+    tf = w.flops_per_token() * w.T / (step / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    out = {"workload": w.name, "T": w.T, "d": w.d, "routed_experts": w.N, "top_k": w.K,
+           "shared_experts": w.K_s, "intermediate": w.I, "dtype": w.dtype,
+           "ms_per_step": round(step, 4), "step_ms": step_stats(per_step),
+           "tokens_per_s": round(w.T / (step / 1e3), 1), "layer_tflops": round(tf, 2),
+           "layer_mfma_frac": round(tf / peak, 4), "gemms": gemm_rooflines(w, stages, peak),
+           "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items() if v[1]}}
+    if cpu_tokens:
+        out["cpu_baseline"] = cpu_baseline(inp, cpu_tokens)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -279,13 +353,12 @@ def main():
     t = upload(inp, dev)
     # the timed steps carry events around GEMM1 only (its launch duration for the
     # roofline); the per-stage breakdown comes from a second pass with every stage
-    ms, g1_stage = time_layer(mx, t, w, args.steps, args.warmup, ["expert_gemm1_swiglu"])
-    _, stages = time_layer(mx, t, w, args.steps, 1, True)
+    ms, per_step, g1_stage = time_layer(mx, t, w, args.steps, args.warmup, ["expert_gemm1_swiglu"])
+    _, _, stages = time_layer(mx, t, w, args.steps, 1, True)
     ms_step = ms / args.steps
     value = w.T * args.steps / (ms / 1e3)
     flops_step = w.flops_per_token() * w.T
     g1_ms, g1_n = g1_stage["expert_gemm1_swiglu"]
-    g2_ms, g2_n = stages["expert_gemm2_down"]
     g1_flops = 4.0 * w.d * w.I * w.T * (w.K + w.K_s)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     g1_tflops = g1_flops / (g1_ms / g1_n / 1e3) / 1e12
@@ -315,21 +388,28 @@ def main():
         dinp = moe_inputs.make(args.decode_workload)
         dw = dinp.w
         dt_ = upload(dinp, dev)
-        dms, _ = time_layer(mx, dt_, dw, args.decode_steps, 10, False)
-        _, dstages = time_layer(mx, dt_, dw, 20, 2, True)
+        dms, dper, _ = time_layer(mx, dt_, dw, args.decode_steps, 10, False)
+        _, _, dstages = time_layer(mx, dt_, dw, 20, 2, True)
         hit = experts_hit(mx, dt_, dw)
         es = 2 if dw.dtype == "bf16" else 4
         dbytes = ((hit + dw.K_s) * 3 * dw.d * dw.I * es + dw.N * dw.d * es
                   + 2 * dw.T * dw.d * es + dw.T * dw.K * 8)
         dstep = dms / args.decode_steps / 1e3
         decode = {"workload": dw.name, "tokens_per_s": round(dw.T / dstep, 1),
-                  "ms_per_step": round(dstep * 1e3, 4), "experts_hit": hit,
+                  "ms_per_step": round(dstep * 1e3, 4), "step_ms": step_stats(dper),
+                  "experts_hit": hit,
                   "algorithmic_bytes": dbytes, "hbm_GBs": round(dbytes / dstep / 1e9, 1),
                   "hbm_frac": round(dbytes / dstep / 1e9 / PEAK_HBM_GBS, 4),
                   "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in dstages.items()
                                if v[1]}}
         del dt_
         torch.cuda.empty_cache()
+
+    # ---- the other prefill-sized workloads (2B-class, 145B-class with skewed routing)
+    others = {}
+    for name, cpu_tokens in ((n, c) for n, c in args.other_workloads if n):
+        others[name] = other_workload(mx, name, args.steps, args.warmup,
+                                      None if args.no_cpu_baseline else cpu_tokens)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_sample_tokens)
 
@@ -341,11 +421,14 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "routed_experts": w.N, "top_k": w.K,
                    "shared_experts": w.K_s, "intermediate": w.I, "accumulate": "f32",
                    "global_batch": w.T, "parallelism": "single GPU"},
+        "step_ms": step_stats(per_step),
         "layer_tflops": round(layer_tflops, 2),
         "layer_mfma_frac": round(layer_tflops / peak, 4),
+        "gemms": gemm_rooflines(w, stages, peak),
         "stage_ms": stage_ms,
         "roofline": roofline,
         "decode": decode,
+        "workloads": others,
         "backward": backward,
         "cpu_baseline": cpu,
     }

@@ -179,6 +179,11 @@ SMALL = {
     # shared one) at a reduced size: I0 = 4096, d = 128
     "gran_m1_ks0_bf16": dict(T=300, d=128, N=16, K=2, K_s=0, I=4096, dtype="bf16", seed=1101),
     "gran_m8_ks1_bf16": dict(T=300, d=128, N=127, K=15, K_s=1, I=512, dtype="bf16", seed=1181),
+    # the ping-pong GEMMs (d, I >= 192): ragged expert tails, partial last n-tiles of
+    # both GEMMs (I = 320: 3 GEMM1 tiles of 128 columns, the last half full; d = 448:
+    # 2 GEMM2 tiles of 256, the last 192 wide), an odd k-step count (I / 64 = 5), two
+    # shared experts whose down projections cross W_down blocks inside one contraction
+    "pp_ragged_bf16": dict(T=700, d=448, N=12, K=3, K_s=2, I=320, dtype="bf16", seed=1301),
     # decode-sized batches (the one-block-per-token router): many experts, a ragged
     # expert count, float32
     "decode_n256_bf16": dict(T=96, d=256, N=256, K=8, K_s=1, I=128, dtype="bf16", seed=1201),
