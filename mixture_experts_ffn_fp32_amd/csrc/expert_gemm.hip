@@ -490,93 +490,72 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 
-// Epilogue through LDS.  bf16 tiles are multiplied with the MFMA operands
-// swapped (weights as the 32-row operand), so lane l holds token row l % 32
-// of each fragment and, in registers 4j..4j+3, four consecutive output
-// columns 8j + 4(l/32) + 0..3: every lane writes 8-byte runs of a staged
-// row-major bf16 tile (16-byte chunk c of row r at chunk c ^ (r & 15)), then
-// every thread copies whole 16-byte row chunks to global memory.  GEMM2
-// tiles are 256 columns wide and go out in two halves.  s_dst[r] is the
-// destination row of tile row r (-1: past the expert's last slot), s_gate[r]
-// its gate.
-template <int MODE, int FM, int THREADS>
-__device__ __forceinline__ void pipe_store_bf16(const ExpertArgs& a, const Tile& ti, int wm, int wn,
-                                                f32x16 (&acc)[FM][4], uint8_t* __restrict__ stage,
-                                                const int* s_dst, const float* s_gate) {
-  constexpr int FN = 4, COLS = 128, CPRW = COLS * 2 / 16;
-  constexpr int PASSES = MODE == 1 ? 1 : 2;
-  const int lane = threadIdx.x & 63, lc = lane & 31, lh = lane >> 5;
+// 16 float32 of one 32 x 32 fragment (MFMA operands swapped: lane l holds
+// token row l % 32 and output columns 8g + 4(l / 32) + 0..3, g = 0..3) ->
+// two 16-byte bf16 runs: after exchanging halves between lanes l and l + 32
+// (v_permlane32_swap), lane l holds columns 0-7 and 16-23 (l < 32) or 8-15
+// and 24-31 (l >= 32).
+__device__ __forceinline__ void pack_runs16(const float (&v)[16], u32x4& r0, u32x4& r1) {
+  uint32_t w[4][2];
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
-    if (MODE == 1 || wn == pass) {
+  for (int g = 0; g < 4; ++g) {
+    w[g][0] = pack_bf16x2(v[4 * g], v[4 * g + 1]);
+    w[g][1] = pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
+  }
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int row = (wm * FM + fm) * 32 + lc;
-        uint8_t* rowp = stage + row * (COLS * 2) + lh * 8;
-        const int sw = row & 15;
-        if (MODE == 1) {
+  for (int q = 0; q < 2; ++q) {
+    const auto s01 = __builtin_amdgcn_permlane32_swap(w[0][q], w[1][q], false, false);
+    const auto s23 = __builtin_amdgcn_permlane32_swap(w[2][q], w[3][q], false, false);
+    w[0][q] = s01[0];
+    w[1][q] = s01[1];
+    w[2][q] = s23[0];
+    w[3][q] = s23[1];
+  }
+  r0 = u32x4{w[0][0], w[0][1], w[1][0], w[1][1]};
+  r1 = u32x4{w[2][0], w[2][1], w[3][0], w[3][1]};
+}
+
+// Epilogue straight from the accumulators (no LDS staging, no barrier): each
+// lane writes two 16-byte runs per fragment of its token rows; s_dst[r] /
+// s_gate[r] give tile row r's destination row (-1: past the expert's last
+// slot) and gate.
+template <int MODE, int FM>
+__device__ __forceinline__ void pipe_store_direct(const ExpertArgs& a, const Tile& ti, int wm,
+                                                  int wn, f32x16 (&acc)[FM][4], const int* s_dst,
+                                                  const float* s_gate) {
+  constexpr int NF = MODE == 1 ? 2 : 4;  // output column groups of 32 per wavefront
+  const int lane = threadIdx.x & 63, hi = lane >> 5;
+  const int lim = MODE == 1 ? a.I : a.d;
 #pragma unroll
-          for (int fn = 0; fn < FN / 2; ++fn)
+  for (int fm = 0; fm < FM; ++fm) {
+    const int row = (wm * FM + fm) * 32 + (lane & 31);
+    const int dst = s_dst[row];
+    uint16_t* rp;
+    if (MODE == 1)
+      rp = ti.routed ? (uint16_t*)a.H_routed + (size_t)max(dst, 0) * a.I
+                     : (uint16_t*)a.H_shared + (size_t)max(dst, 0) * a.K_s * a.I +
+                           (size_t)(ti.v - a.N) * a.I;
+    else
+      rp = (ti.routed ? (uint16_t*)a.Y : (uint16_t*)a.Y_shared) + (size_t)max(dst, 0) * a.d;
+    const float g = MODE == 2 ? s_gate[row] : 1.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int c = (wn * (FN / 2) + fn) * 4 + j;
-              const f32x16& gt = acc[fm][fn];
-              const f32x16& up = acc[fm][fn + FN / 2];
-              uint2 w;
-              w.x = pack_bf16x2(silu_mul(gt[4 * j], up[4 * j]), silu_mul(gt[4 * j + 1], up[4 * j + 1]));
-              w.y = pack_bf16x2(silu_mul(gt[4 * j + 2], up[4 * j + 2]),
-                                silu_mul(gt[4 * j + 3], up[4 * j + 3]));
-              *(uint2*)(rowp + ((c ^ sw) << 4)) = w;
-            }
-        } else {
-          const float g = s_gate[row];
+    for (int f = 0; f < NF; ++f) {
+      float v[16];
+      if (MODE == 1) {
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
+        for (int r = 0; r < 16; ++r) v[r] = silu_mul(acc[fm][f][r], acc[fm][f + 2][r]);
+      } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int c = fn * 4 + j;
-              const f32x16& y = acc[fm][fn];
-              uint2 w;
-              w.x = pack_bf16x2(y[4 * j] * g, y[4 * j + 1] * g);
-              w.y = pack_bf16x2(y[4 * j + 2] * g, y[4 * j + 3] * g);
-              *(uint2*)(rowp + ((c ^ sw) << 4)) = w;
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < 16; ++r) v[r] = acc[fm][f][r] * g;
+      }
+      u32x4 r0, r1;
+      pack_runs16(v, r0, r1);  // every lane takes part in the exchange
+      const int col = ti.n0 + (wn * NF + f) * 32;
+      if (dst >= 0 && col < lim) {
+        *(u32x4*)(rp + col + 8 * hi) = r0;
+        *(u32x4*)(rp + col + 16 + 8 * hi) = r1;
       }
     }
-    lds_sync();
-    // thread t copies chunk t % 16 of rows t / 16 + k * (THREADS / 16)
-    constexpr int RSTEP = THREADS / CPRW, NR = kPipeBM / RSTEP;
-    constexpr int NB = 4;  // rows in flight per thread
-    static_assert(NR % NB == 0, "whole batches");
-    const int c = threadIdx.x % CPRW, r0 = threadIdx.x / CPRW;
-    uint16_t* base;
-    size_t pitch;
-    if (MODE == 1) {
-      base = ti.routed ? (uint16_t*)a.H_routed + ti.n0
-                       : (uint16_t*)a.H_shared + (size_t)(ti.v - a.N) * a.I + ti.n0;
-      pitch = ti.routed ? (size_t)a.I : (size_t)a.K_s * a.I;
-    } else {
-      base = (ti.routed ? (uint16_t*)a.Y : (uint16_t*)a.Y_shared) + ti.n0 + pass * COLS;
-      pitch = (size_t)a.d;
-    }
-#pragma unroll
-    for (int k0 = 0; k0 < NR; k0 += NB) {
-      int drow[NB];
-      u32x4 v[NB];
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const int row = r0 + (k0 + k) * RSTEP;
-        drow[k] = s_dst[row];
-        v[k] = *(const u32x4*)(stage + row * (COLS * 2) + ((c ^ (row & 15)) << 4));
-      }
-      const bool col_ok = ti.n0 + (MODE == 1 ? 0 : pass * COLS) + c * 8 < (MODE == 1 ? a.I : a.d);
-#pragma unroll
-      for (int k = 0; k < NB; ++k)
-        if (drow[k] >= 0 && col_ok) *(u32x4*)(base + (size_t)drow[k] * pitch + c * 8) = v[k];
-    }
-    lds_sync();
   }
 }
 
@@ -606,7 +585,7 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   constexpr int BNO = MODE == 1 ? kPipeBNB / 2 : kPipeBNB;
   constexpr int kStep = kPipeRB / (int)sizeof(Tp);
   constexpr int NINST = Cfg::kNinst, FM = Cfg::FM;
-  constexpr bool kStaged = std::is_same<E, ElemBF16>::value;
+  constexpr bool kDirect = std::is_same<E, ElemBF16>::value;  // bf16: epilogue from registers
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kPipeSlot];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kPipeSlot];
   __shared__ int s_tab[kMaxV + 1];
@@ -732,14 +711,15 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
                             lds0 + wave * NINST * 1024);
     }
 
-    // epilogue: slot 1 is free once every wavefront has finished its last reads
+    // epilogue: each tile row's destination and gate, through LDS
     if (tid < kPipeBM) {
       s_dst[tid] = my_dst;
       s_gate[tid] = my_gate;
     }
     lds_sync();
-    if constexpr (kStaged) {
-      pipe_store_bf16<MODE, FM, Cfg::kThreads>(a, ti, wm, wn, acc, lds1, s_dst, s_gate);
+    if constexpr (kDirect) {
+      pipe_store_direct<MODE, FM>(a, ti, wm, wn, acc, s_dst, s_gate);
+      lds_sync();  // s_dst / s_gate are rewritten for the next tile
     } else {
       store_tile<E, MODE, FM, 4>(a, ti, wm, wn, acc);
       __syncthreads();
