@@ -5,14 +5,10 @@
 // largest s of each token are kept as its gates, the rest are zero.  Ties
 // are broken towards the lower expert index so that exactly K are kept.
 //
-// Layout of the work: one block = 64 tokens = 4 wavefronts x 16 tokens.
-// Token rows and expert rows are staged through two LDS buffers, up to 512
-// bytes of each row per stage.  A
-// wavefront computes the logits of its 16 tokens against all N experts
-// (padded to 16F) with 16x16 MFMA tiles, then each group of 16 lanes owns one
-// token at a time (the MFMA output puts token rows on lane groups and
-// experts on lanes), so softmax and top-K reductions are 4-step butterflies
-// inside a 16-lane group.  Logits never leave registers.
+// Layout of the work: one block = 32 tokens x all experts, 4 wavefronts
+// (two token groups x two expert halves), several stages of the token and
+// expert rows in flight (see router_kernel); batches of at most 128 tokens
+// take a one-block-per-token kernel (router_small_kernel).
 #include <cstdlib>
 
 #include "moe_internal.h"
@@ -62,10 +58,19 @@ __device__ __forceinline__ int router_lds_offset(int r, int c) {
   return r * (CH * 16) + ((c ^ (r & 15)) << 4);
 }
 
-// F: experts padded to 16F.  CH: 16-byte chunks of each row loaded per
-// k-step (long k-steps keep many loads in flight per wavefront: the kernel
-// is bound by the latency of reading u once).  TB = 64 tokens per block,
-// wavefront w computing tokens 16w .. 16w + 15 against every expert.
+// One block = 32 tokens x all experts (padded to NP = 16F, F even), four
+// wavefronts: wavefront w multiplies token group w & 1 (16 tokens) against
+// expert half w >> 1 (F / 2 fragments of 16), 16x16x32 bf16 MFMAs (16x16x4
+// for float32) with float32 accumulation.  A stage is CH 16-byte chunks of
+// every token row and expert row; the loads of P stages are in flight at
+// once in registers (each thread moves PASSES chunks per stage), and a stage
+// is written to one of two LDS buffers just before it is multiplied, so the
+// block is bound by the rate it reads u and E_gate rather than by one memory
+// round trip per stage.  After the last stage every wavefront writes its
+// logits to LDS and each 16-lane row group takes one token at a time for the
+// softmax and top-K: 4-step DPP butterflies inside the row group.
+constexpr int kRouterTB = 32;
+
 template <class E, int F, int CH>
 __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __restrict__ u,
                                                      const typename E::T* __restrict__ Eg,
@@ -74,84 +79,93 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
                                                      float* __restrict__ gate,
                                                      float* __restrict__ scores) {
   using Tp = typename E::T;
-  constexpr int TB = 64;                // tokens per block
+  constexpr int TB = kRouterTB;
   constexpr int NP = 16 * F;            // experts, padded
-  constexpr int ROWS = TB + NP;         // LDS rows per stage: tokens, then experts
+  constexpr int FW = F / 2;             // expert fragments per wavefront
+  constexpr int ROWS = TB + NP;         // rows per stage: tokens, then experts
   constexpr int RPP = 256 / CH;         // rows covered by one pass of the block
-  constexpr int PASSES = (ROWS + RPP - 1) / RPP;
+  constexpr int PASSES = ROWS / RPP;    // 16-byte loads per thread per stage
+  constexpr int P = PASSES * 4 <= 40 ? 4 : PASSES * 3 <= 40 ? 3 : PASSES * 2 <= 40 ? 2 : 1;
+  static_assert(F % 2 == 0 && ROWS % RPP == 0, "stage shape");
+  constexpr int kStep = CH * E::kPerChunk;  // contraction elements per stage
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][ROWS * CH * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * TB;
-  const int tg = wave;                  // the wavefront's group of 16 tokens
-  constexpr int kStep = CH * E::kPerChunk;  // contraction elements per stage
+  const int tg = wave & 1, fh = wave >> 1;
   const int nsteps = d / kStep;
 
-  // Each thread moves chunk c of rows tid / CH + RPP * i.  Rows past T or N
-  // are clamped to a valid row; their results are never written.
+  // each thread moves chunk c of rows tid / CH + RPP * i; rows past T or N
+  // are clamped to a valid row (their results are never written)
   const int c = tid % CH;
   const Tp* rowp[PASSES];
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
     const int r = tid / CH + RPP * i;
-    if (r < TB) {
-      rowp[i] = u + (size_t)min(t0 + r, T - 1) * d;
-    } else {
-      rowp[i] = Eg + (size_t)min(max(r - TB, 0), N - 1) * d;
-    }
+    rowp[i] = r < TB ? u + (size_t)min(t0 + r, T - 1) * d
+                     : Eg + (size_t)min(r - TB, N - 1) * d;
   }
-  u32x4 stage[PASSES];
-  auto gload = [&](int s) {
+  u32x4 stage[P][PASSES];
+  auto issue = [&](int s, u32x4 (&st)[PASSES]) {
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int r = tid / CH + RPP * i;
-      if (r < ROWS) stage[i] = *(const u32x4*)(rowp[i] + s * kStep + c * E::kPerChunk);
-    }
+    for (int i = 0; i < PASSES; ++i) st[i] = *(const u32x4*)(rowp[i] + (size_t)s * kStep + c * E::kPerChunk);
   };
-  auto lstore = [&](int buf) {
+  f32x4 acc[FW];
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int r = tid / CH + RPP * i;
-      if (r < ROWS) *(u32x4*)(lds[buf] + router_lds_offset<CH>(r, c)) = stage[i];
-    }
-  };
+  for (int f = 0; f < FW; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  f32x4 acc[F];
 #pragma unroll
-  for (int f = 0; f < F; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
+  for (int j = 0; j < P; ++j)
+    if (j < nsteps) issue(j, stage[j]);
+  for (int s0 = 0; s0 < nsteps; s0 += P) {
 #pragma unroll
-    for (int kg = 0; kg < CH / 4; ++kg) {  // k-groups of 4 chunks
-      const int ch = kg * 4 + (lane >> 4);
-      const u32x4 a = *(const u32x4*)(lds[buf] + router_lds_offset<CH>(tg * 16 + (lane & 15), ch));
+    for (int j = 0; j < P; ++j) {
+      const int s = s0 + j;
+      if (s < nsteps) {
+        uint8_t* buf = lds[s & 1];
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const u32x4 b =
-            *(const u32x4*)(lds[buf] + router_lds_offset<CH>(TB + f * 16 + (lane & 15), ch));
-        acc[f] = mfma16(E{}, a, b, acc[f]);
+        for (int i = 0; i < PASSES; ++i)
+          *(u32x4*)(buf + router_lds_offset<CH>(tid / CH + RPP * i, c)) = stage[j][i];
+        if (s + P < nsteps) issue(s + P, stage[j]);
+        __syncthreads();
+#pragma unroll
+        for (int kg = 0; kg < CH / 4; ++kg) {  // k-groups of 4 chunks
+          const int ch = kg * 4 + (lane >> 4);
+          const u32x4 av = *(const u32x4*)(buf + router_lds_offset<CH>(tg * 16 + (lane & 15), ch));
+#pragma unroll
+          for (int f = 0; f < FW; ++f) {
+            const u32x4 bv =
+                *(const u32x4*)(buf + router_lds_offset<CH>(TB + (fh * FW + f) * 16 + (lane & 15), ch));
+            acc[f] = mfma16(E{}, av, bv, acc[f]);
+          }
+        }
       }
     }
-    if (s + 1 < nsteps) lstore(buf ^ 1);
-    __syncthreads();
   }
 
-  // acc[f][r]: token row tg*16 + 4*(lane/16) + r, expert f*16 + lane%16.
+  // acc[f][r]: token tg*16 + 4*(lane/16) + r, expert (fh*FW + f)*16 + lane%16.
+  constexpr int LP = NP + 1;  // padded logit row (floats)
+  static_assert(TB * LP * 4 <= (int)sizeof(lds), "logits fit the stage buffers");
+  float* lg = (float*)&lds[0][0];
+  __syncthreads();  // every wavefront's last reads of the stage buffers are done
+#pragma unroll
+  for (int f = 0; f < FW; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      lg[(tg * 16 + 4 * (lane >> 4) + r) * LP + (fh * FW + f) * 16 + (lane & 15)] = acc[f][r];
+  __syncthreads();
+  // softmax and top-K: row group grp of wavefront w takes tokens 8w + 4q + grp
   const int grp = lane >> 4, col = lane & 15;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = t0 + tg * 16 + grp * 4 + r;
+  for (int q = 0; q < 2; ++q) {
+    const int tl = wave * 8 + q * 4 + grp;
+    const int t = t0 + tl;
     float v[F];
     float m = -INFINITY;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int e = f * 16 + col;
-      v[f] = (e < N) ? acc[f][r] + (bias ? bias[e] : 0.f) : -INFINITY;
+      v[f] = (e < N) ? lg[tl * LP + e] + (bias ? bias[e] : 0.f) : -INFINITY;
       m = fmaxf(m, v[f]);
     }
     m = fmaxf(m, row16_exchange<0>(m));
@@ -357,20 +371,18 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
   }
 }
 
-// One block per 64 tokens (measured fastest against 16- and 32-token blocks
-// that split the experts over wavefronts: each block is bound by the latency
-// of its k-steps, not by the number of blocks).
+// The widest stage the row length allows (fewer, longer stages for few experts).
 template <class E, int F>
 hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int T, int d, int N,
                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
   using Tp = typename E::T;
-  const dim3 grid((T + 63) / 64), block(256);
+  const dim3 grid((T + kRouterTB - 1) / kRouterTB), block(256);
   const Tp* up = (const Tp*)u;
   const Tp* ep = (const Tp*)Eg;
-  // long k-steps (two stages of (64 + 16F) rows in LDS) where d allows
-  constexpr int CH = F <= 4 ? 32 : F == 8 ? 16 : 8;
-  if ((size_t)d * sizeof(Tp) % (CH * 16) == 0)
-    router_kernel<E, F, CH><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
+  const size_t row = (size_t)d * sizeof(Tp);
+  constexpr int CHW = F <= 4 ? 32 : F == 8 ? 16 : 8;  // chunks per stage the registers allow
+  if (row % (CHW * 16) == 0)
+    router_kernel<E, F, CHW><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
   else
     router_kernel<E, F, 8><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
   return hipGetLastError();
@@ -392,7 +404,6 @@ hipError_t launch_router_t(const void* u, const void* Eg, const float* bias, int
                                               gate, scores);
     return hipGetLastError();
   }
-  if (N <= 16) return launch_router_f<E, 1>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
   if (N <= 32) return launch_router_f<E, 2>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
   if (N <= 64) return launch_router_f<E, 4>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
   if (N <= 128) return launch_router_f<E, 8>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
