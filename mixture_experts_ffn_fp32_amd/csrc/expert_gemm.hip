@@ -179,8 +179,10 @@ __device__ __forceinline__ const typename E::T* tile_row_ptr(const ExpertArgs& a
 template <int MODE>
 __device__ __forceinline__ size_t b_offset(const ExpertArgs& a, const Tile& ti, size_t k0) {
   if (MODE == 2 && !ti.routed) {
-    const size_t Id = (size_t)a.I * a.d;
-    return k0 + (k0 / a.I) * (3 * Id - a.I);
+    // 32-bit quotient (k0 < K_s * I < 2^31): a 64-bit one is a long scalar
+    // sequence, and this runs at every k-step of a shared tile
+    const uint32_t kb = (uint32_t)k0 / (uint32_t)a.I;
+    return k0 + (size_t)kb * (3 * (size_t)a.I * a.d - a.I);
   }
   return k0;
 }
@@ -617,7 +619,8 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   const bool split = MODE == 2 && a.K_s > 1 && S > 0;
   const int X = min(8, (int)gridDim.x);
   const int x = blockIdx.x % X, lb = blockIdx.x / X;
-  auto part = [&](int n, int y) { return (int)((long long)n * y / X); };
+  // 32-bit arithmetic: the host's operand bounds keep n * 8 far below 2^32
+  auto part = [&](int n, int y) { return (int)((unsigned)n * (unsigned)y / (unsigned)X); };
   auto n_of = [&](int y) -> int {  // tiles in XCD y's share
     return split ? (part(S, y + 1) - part(S, y)) + (part(Lr, y + 1) - part(Lr, y))
                  : part(total, y + 1) - part(total, y);
