@@ -42,9 +42,9 @@ constexpr int kBtMaxV = 256 + 16;
 
 __host__ __device__ constexpr int bt_bn(int G) { return G == BT_AC ? kBtBNB / 2 : kBtBNB; }
 
-struct BtGroup {
+struct BtGroup {  // (all int: a bool member's padding would be copied through memory)
   int M, Nc, steps, rows, base;
-  bool routed;
+  int routed;  // 0 or 1
 };
 
 // Geometry of virtual expert v in product G.
@@ -52,7 +52,7 @@ template <int G>
 __device__ __forceinline__ BtGroup bt_group(const BwdArgs& a, int v) {
   BtGroup g;
   const int TK = a.T * a.K;
-  g.routed = v < a.N;
+  g.routed = v < a.N ? 1 : 0;
   if (g.routed) {
     g.base = min(max(a.offsets[v], 0), TK);
     g.rows = min(max(a.offsets[v + 1], g.base), TK) - g.base;

@@ -62,9 +62,12 @@ __global__ __launch_bounds__(64) void tile_table_kernel(const int32_t* __restric
 // ---------------------------------------------------------------- shared pieces
 // The tile of one block: virtual expert v, its first output column n0, first
 // row m0, and the expert's slot range.
+// (All int: a bool member leaves padding bytes that a struct copy moves
+// through per-thread memory, which the compiler may place in LDS and then
+// wait for every direct-to-LDS load in flight before touching.)
 struct Tile {
   int v, n0, m0, row_base, rows;
-  bool routed;
+  int routed;  // 0 or 1
 };
 
 // Maps the block to its tile through the tile table (m fastest within an
@@ -92,7 +95,7 @@ __device__ __forceinline__ bool find_tile(const ExpertArgs& a, int* s_tab, int* 
   ti.v = v;
   ti.n0 = (local / mt_v) * BNO;
   ti.m0 = (local % mt_v) * BM;
-  ti.routed = v < a.N;
+  ti.routed = v < a.N ? 1 : 0;
   const int TK = a.T * a.K;
   ti.row_base = 0;
   ti.rows = a.T;
@@ -114,8 +117,11 @@ __device__ __forceinline__ int load_tile_table(const ExpertArgs& a, int* s_tab) 
 }
 
 // Tile L of the table in LDS (every thread searches the same entries: no barrier).
-template <int BM, int BNO, int MODE>
-__device__ __forceinline__ Tile tile_of(const ExpertArgs& a, const int* s_tab, int V, int L) {
+// kLdsOff: the dispatch offsets are read from an LDS copy `s_off` (no global
+// load, whose wait would also wait for every load in flight).
+template <int BM, int BNO, int MODE, bool kLdsOff = false>
+__device__ __forceinline__ Tile tile_of(const ExpertArgs& a, const int* s_tab, int V, int L,
+                                        const int* s_off = nullptr) {
   const int nt = ((MODE == 1 ? a.I : a.d) + BNO - 1) / BNO;  // the last n-tile may be partial
   int lo = 0, hi = V - 1;  // largest v with s_tab[v] * nt <= L
   while (lo < hi) {
@@ -131,13 +137,15 @@ __device__ __forceinline__ Tile tile_of(const ExpertArgs& a, const int* s_tab, i
   ti.v = v;
   ti.n0 = (local / mt_v) * BNO;
   ti.m0 = (local % mt_v) * BM;
-  ti.routed = v < a.N;
+  ti.routed = v < a.N ? 1 : 0;
   const int TK = a.T * a.K;
   ti.row_base = 0;
   ti.rows = a.T;
   if (ti.routed) {
-    ti.row_base = min(max(a.offsets[v], 0), TK);
-    ti.rows = min(max(a.offsets[v + 1], ti.row_base), TK) - ti.row_base;
+    const int o0 = kLdsOff ? s_off[v] : a.offsets[v];
+    const int o1 = kLdsOff ? s_off[v + 1] : a.offsets[v + 1];
+    ti.row_base = min(max(o0, 0), TK);
+    ti.rows = min(max(o1, ti.row_base), TK) - ti.row_base;
   }
   return ti;
 }
@@ -391,16 +399,35 @@ __device__ __forceinline__ Tile uni(const Tile& t) {
   u.m0 = uni(t.m0);
   u.row_base = uni(t.row_base);
   u.rows = uni(t.rows);
-  u.routed = uni((int)t.routed) != 0;
+  u.routed = uni(t.routed);
   return u;
 }
 
 template <class E, int MODE, int NI>
 __device__ __forceinline__ void pipe_prepare(const ExpertArgs& a, const Tile& ti, int wave,
-                                             int lane, PipeLoads<NI>& ld) {
+                                             int lane, bool is_a, PipeLoads<NI>& ld) {
   ld.b_row0 = uni((const uint8_t*)tile_row_ptr<E, MODE, kPipeBM, kPipeBNB>(a, ti, kPipeBM));
   ld.a_base = uni(MODE == 1 ? (const uint8_t*)a.u
                             : (const uint8_t*)(ti.routed ? a.H_routed : a.H_shared));
+  if (MODE == 1 && ti.routed && is_a) {
+    // gathered token rows: every row's pair index is requested before any
+    // is used, so the lookups cost one round trip, not one each
+    const int TK = a.T * a.K;
+    int pr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (wave * NI + i) * 8 + (lane >> 3);
+      pr[i] = a.sorted_pair[ti.row_base + min(ti.m0 + r, ti.rows - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (wave * NI + i) * 8 + (lane >> 3);
+      const uint32_t tok = (unsigned)pr[i] < (unsigned)TK ? (unsigned)pr[i] / (unsigned)a.K : 0u;
+      const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+      ld.off[i] = tok * (uint32_t)a.d * (uint32_t)sizeof(typename E::T) + chunk * 16;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = (wave * NI + i) * 8 + (lane >> 3);
@@ -517,21 +544,20 @@ __device__ __forceinline__ void pack_runs16(const float (&v)[16], u32x4& r0, u32
   r1 = u32x4{w[2][0], w[2][1], w[3][0], w[3][1]};
 }
 
-// Epilogue straight from the accumulators (no LDS staging, no barrier): each
-// lane writes two 16-byte runs per fragment of its token rows; s_dst[r] /
-// s_gate[r] give tile row r's destination row (-1: past the expert's last
-// slot) and gate.
+// Epilogue straight from the accumulators (no LDS, no barrier): each lane
+// writes two 16-byte runs per fragment of its token rows; dst[fm] / g[fm]
+// are the destination row (-1: past the expert's last slot) and gate of the
+// lane's row (wm * FM + fm) * 32 + lane % 32.
 template <int MODE, int FM>
 __device__ __forceinline__ void pipe_store_direct(const ExpertArgs& a, const Tile& ti, int wm,
-                                                  int wn, f32x16 (&acc)[FM][4], const int* s_dst,
-                                                  const float* s_gate) {
+                                                  int wn, f32x16 (&acc)[FM][4],
+                                                  const int (&dsts)[FM], const float (&gates)[FM]) {
   constexpr int NF = MODE == 1 ? 2 : 4;  // output column groups of 32 per wavefront
   const int lane = threadIdx.x & 63, hi = lane >> 5;
   const int lim = MODE == 1 ? a.I : a.d;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    const int row = (wm * FM + fm) * 32 + (lane & 31);
-    const int dst = s_dst[row];
+    const int dst = dsts[fm];
     uint16_t* rp;
     if (MODE == 1)
       rp = ti.routed ? (uint16_t*)a.H_routed + (size_t)max(dst, 0) * a.I
@@ -539,7 +565,7 @@ __device__ __forceinline__ void pipe_store_direct(const ExpertArgs& a, const Til
                            (size_t)(ti.v - a.N) * a.I;
     else
       rp = (ti.routed ? (uint16_t*)a.Y : (uint16_t*)a.Y_shared) + (size_t)max(dst, 0) * a.d;
-    const float g = MODE == 2 ? s_gate[row] : 1.f;
+    const float g = MODE == 2 ? gates[fm] : 1.f;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       float v[16];
@@ -561,23 +587,37 @@ __device__ __forceinline__ void pipe_store_direct(const ExpertArgs& a, const Til
   }
 }
 
-// Destination row (and gate) of tile row r: H slot / pair index / token, or -1.
+// Destination row of tile row r (H slot / token, or -1 past the expert's
+// last slot); for GEMM2's routed rows the raw pair index, looked up here and
+// checked by pipe_row_gate after the next barrier (nothing waits for the
+// load in between).
 template <int MODE>
-__device__ __forceinline__ void pipe_row_dest(const ExpertArgs& a, const Tile& ti, int r, int& dst,
-                                              float& g) {
+__device__ __forceinline__ int pipe_row_dest(const ExpertArgs& a, const Tile& ti, int r) {
   const int p = ti.m0 + r;
+  if (p >= ti.rows) return -1;
+  if (MODE == 1 || !ti.routed) return (MODE == 1 && ti.routed) ? ti.row_base + p : p;
+  return a.sorted_pair[ti.row_base + p];
+}
+
+// GEMM2's routed rows: the pair index brought into range and its gate.
+template <int MODE>
+__device__ __forceinline__ void pipe_row_gate(const ExpertArgs& a, const Tile& ti, int r, int& dst,
+                                              float& g) {
   g = 1.f;
-  dst = -1;
-  if (p >= ti.rows) return;
-  if (MODE == 1 || !ti.routed) {
-    dst = (MODE == 1 && ti.routed) ? ti.row_base + p : p;
-    return;
-  }
+  if (MODE == 1 || !ti.routed || ti.m0 + r >= ti.rows) return;
   const int TK = a.T * a.K;
-  int pair = a.sorted_pair[ti.row_base + p];
-  pair = ((unsigned)pair < (unsigned)TK) ? pair : 0;
-  dst = pair;
-  g = a.gate[pair];
+  dst = ((unsigned)dst < (unsigned)TK) ? dst : 0;
+  g = a.gate[dst];
+}
+
+// The claim of a tile from a share's counter, issued by one lane.  The
+// address is made to look lane-varying so that the compiler does not turn
+// the atomic into a wavefront reduction whose broadcast waits for the reply
+// at once: the reply is awaited at the next barrier's wait instead.
+__device__ __forceinline__ int claim_issue(int* ctr) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return atomicAdd(ctr + z, 1);
 }
 
 template <class E, int MODE, int W>
@@ -591,8 +631,7 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kPipeSlot];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kPipeSlot];
   __shared__ int s_tab[kMaxV + 1];
-  __shared__ int s_dst[kPipeBM];
-  __shared__ __attribute__((aligned(16))) float s_gate[kPipeBM];
+  __shared__ int s_off[kMaxV + 1];
   __shared__ int s_claim;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -611,7 +650,8 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
   // them.  Each block takes one tile by its index in its XCD's share, then
   // claims the next one from the share's counter; when its XCD has none
   // left it claims from the other XCDs' (the XCDs run at different clocks).
-  const int V = load_tile_table<MODE>(a, s_tab);
+  for (int i = tid; i <= a.N; i += blockDim.x) s_off[i] = a.offsets[i];
+  const int V = load_tile_table<MODE>(a, s_tab);  // (its barrier also covers s_off)
   const int nt = ((MODE == 1 ? a.I : a.d) + BNO - 1) / BNO;
   const int total = s_tab[V] * nt;
   const int Lr = MODE == 2 ? s_tab[a.N] * nt : total;  // tiles before the shared ones
@@ -633,29 +673,56 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
     return part(total, y) + p;
   };
   int* const ctr = a.counters + (MODE - 1) * 8;
-  // the next tile: from the own XCD's counter first, then the others' (-1: none)
-  auto claim_next = [&]() -> int {
-    for (int k = 0; k < X; ++k) {
+  // position p of XCD y's share given counter reply c (the first blocks took
+  // their tiles by index)
+  auto pos = [&](int y, int c) { return ((int)gridDim.x - y + X - 1) / X + c; };
+  // the next tile from the other XCDs' counters (-1: none), replies awaited one by one
+  auto claim_others = [&]() -> int {
+    for (int k = 1; k < X; ++k) {
       const int y = x + k < X ? x + k : x + k - X;
-      const int p = ((int)gridDim.x - y + X - 1) / X + atomicAdd(ctr + y, 1);
+      const int p = pos(y, atomicAdd(ctr + y, 1));
       if (p < n_of(y)) return map(y, p);
     }
     return -1;
   };
+  // the tile of the own XCD's counter reply c, else one of the others'
+  auto claim_resolve = [&](int c) -> int {
+    const int p = pos(x, c);
+    return p < n_of(x) ? map(x, p) : claim_others();
+  };
   int L = lb < n_of(x) ? map(x, lb) : -1;
   if (L < 0) {
-    if (tid == 0) s_claim = claim_next();
+    if (tid == 0) s_claim = claim_resolve(atomicAdd(ctr + x, 1));
     __syncthreads();
     L = uni(s_claim);
     __syncthreads();  // read by all before the first tile's claim rewrites it
     if (L < 0) return;
   }
 
-  Tile ti = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, L));
+  Tile ti = uni(tile_of<kPipeBM, BNO, MODE, true>(a, s_tab, V, L, s_off));
   PipeLoads<NINST> ld;
-  pipe_prepare<E, MODE>(a, ti, wave, lane, ld);
+  pipe_prepare<E, MODE>(a, ti, wave, lane, is_a, ld);
   pipe_issue<E, MODE>(a, ti, ld, 0, is_a, lds0 + wave * NINST * 1024);
 
+  f32x16 acc[FM][4];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  zero_acc();
+  // Destination row and gate of this lane's rows (wm * FM + fm) * 32 +
+  // lane % 32, in registers until the epilogue.  bf16: a tile's results are
+  // written after the next tile's first barrier (its first k-step has
+  // landed), so that the wait for that k-step's loads does not also wait for
+  // the stores; until then they stay in acc, dst and gate.
+  int dst[FM];
+  float gate[FM];
+  bool pending = false;
+  Tile tp = ti;
   while (true) {
     const int Kc = MODE == 1 ? a.d : (ti.routed ? a.I : a.K_s * a.I);
     // an odd k-step count is padded with one k-step of zeros (loaded as out
@@ -665,36 +732,35 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
     // A wavefront whose rows all lie past the expert's last slot skips its
     // MFMAs (the other wavefront on its SIMD gets the MFMA unit).
     const bool active = ti.m0 + wm * FM * 32 < ti.rows;
-    // The block's next tile, needed at the last k-step, is claimed at the end
-    // of the first k-step: the wait for the counter's reply then coincides
-    // with the wait for that k-step's loads (with only two k-steps it is
-    // claimed at once).
-    int claim = -1;
-    if (nsteps == 2 && tid == 0) claim = claim_next();
+    // The block's next tile, needed at the last k-step, is claimed during
+    // the first k-step (the counter's reply is awaited with the second
+    // k-step's loads) and published in s_claim at the last pair; with only
+    // two k-steps it is claimed at once.
+    int claim = -1, reply = 0;
+    if (nsteps == 2 && tid == 0) claim = claim_resolve(atomicAdd(ctr + x, 1));
     int Ln = -1;
     bool has_next = false;
-    // destination row and gate of tile row `tid`, kept in registers until the epilogue
-    int my_dst = -1;
-    float my_gate = 1.f;
-    if (tid < kPipeBM) pipe_row_dest<MODE>(a, ti, tid, my_dst, my_gate);
-
-    f32x16 acc[FM][4];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     Tile tn = ti;
     for (int s = 0; s < nsteps; s += 2) {
       if (s + 2 >= nsteps && tid == 0) s_claim = claim;
       // even k-step: slot 0 holds k-step s; k-step s + 1 goes to slot 1
       pipe_sync();
+      if (s == 0) {
+        if (kDirect && pending) {  // the previous tile's results
+          pipe_store_direct<MODE, FM>(a, tp, wm, wn, acc, dst, gate);
+          zero_acc();
+        }
+        // this tile's rows (GEMM2: the pair index now, its gate after the
+        // next barrier, which awaits the lookup with the k-step's loads)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) dst[fm] = pipe_row_dest<MODE>(a, ti, (wm * FM + fm) * 32 + (lane & 31));
+        if (!kDirect) zero_acc();
+      }
       pipe_mma<E, MODE, FM>(lds0, wm, wn, lane, acc, active,
                             pipe_dma_base<E, MODE>(a, ti, ld, s + 1 < nreal ? s + 1 : 0, is_a),
                             ld.off, lds1 + wave * NINST * 1024, s + 1 < nreal ? 0x7fffffff : 0);
-      if (s == 0 && nsteps > 2 && tid == 0) claim = claim_next();
+      if (s == 0 && nsteps > 2 && tid == 0) reply = claim_issue(ctr + x);
       // odd k-step: slot 1 holds k-step s + 1; slot 0 gets k-step s + 2, or
       // the next tile's first k-step after the last one
       if (s + 2 >= nsteps) {
@@ -702,10 +768,16 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
         has_next = Ln >= 0;
       }
       if (s + 2 >= nsteps && has_next) {
-        tn = uni(tile_of<kPipeBM, BNO, MODE>(a, s_tab, V, Ln));
-        pipe_prepare<E, MODE>(a, tn, wave, lane, ld);  // this tile's loads are all issued
+        tn = uni(tile_of<kPipeBM, BNO, MODE, true>(a, s_tab, V, Ln, s_off));
+        pipe_prepare<E, MODE>(a, tn, wave, lane, is_a, ld);  // this tile's loads are all issued
       }
       pipe_sync();
+      if (s == 0) {
+        if (nsteps > 2 && tid == 0) claim = claim_resolve(reply);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          pipe_row_gate<MODE>(a, ti, (wm * FM + fm) * 32 + (lane & 31), dst[fm], gate[fm]);
+      }
       // after the last k-step: the next tile's first k-step, or (last tile)
       // the first k-step again into the slot nobody reads any more
       const uint8_t* db2 = s + 2 < nsteps ? pipe_dma_base<E, MODE>(a, ti, ld, s + 2, is_a)
@@ -714,16 +786,15 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
                             lds0 + wave * NINST * 1024);
     }
 
-    // epilogue: each tile row's destination and gate, through LDS
-    if (tid < kPipeBM) {
-      s_dst[tid] = my_dst;
-      s_gate[tid] = my_gate;
-    }
-    lds_sync();
     if constexpr (kDirect) {
-      pipe_store_direct<MODE, FM>(a, ti, wm, wn, acc, s_dst, s_gate);
-      lds_sync();  // s_dst / s_gate are rewritten for the next tile
+      if (has_next) {
+        pending = true;  // written after the next tile's first barrier
+        tp = ti;
+      } else {
+        pipe_store_direct<MODE, FM>(a, ti, wm, wn, acc, dst, gate);
+      }
     } else {
+      lds_sync();
       store_tile<E, MODE, FM, 4>(a, ti, wm, wn, acc);
       __syncthreads();
     }
