@@ -5,8 +5,9 @@
 // sec. 3.2 layer equation).  The gates were applied when Y was written, so
 // this is a deterministic gather: each thread owns one 16-byte chunk of a
 // row of h, reads the matching chunks of u, Y_shared and the token's K rows
-// of Y (contiguous, token-major), sums in float32 in that fixed order and
-// rounds once.  HBM-bound: (K + 2) reads and one write per output element.
+// of Y (contiguous, token-major), all in flight at once, sums in float32 in
+// that fixed order and rounds once.  HBM-bound: (K + 2) reads and one write
+// per output element.
 #include "moe_internal.h"
 
 namespace moe {
@@ -26,24 +27,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const typename E::T* __res
   const int t = (int)(chunk / cpr);
   const int col = (int)(chunk % cpr) * V;
 
+  // every row of the token is requested before any is added (in groups of
+  // eight Y rows; the sum keeps the fixed order u, Y_shared, Y_0 .. Y_{K-1})
+  constexpr int G = 8;
+  const Tp* yr = Y + (size_t)t * K * d + col;
+  u32x4 xu = *(const u32x4*)(u + (size_t)t * d + col);
+  u32x4 xs = Ys != nullptr ? *(const u32x4*)(Ys + (size_t)t * d + col) : u32x4{0u, 0u, 0u, 0u};
+  u32x4 xy[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    if (j < K) xy[j] = *(const u32x4*)(yr + (size_t)j * d);
   float acc[V];
-  {
-    const u32x4 x = *(const u32x4*)(u + (size_t)t * d + col);
-    const Tp* xs = (const Tp*)&x;
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[j] = load_as_f32<E>(xs + j);
-  }
+  for (int j = 0; j < V; ++j) acc[j] = load_as_f32<E>((const Tp*)&xu + j);
   if (Ys != nullptr) {
-    const u32x4 x = *(const u32x4*)(Ys + (size_t)t * d + col);
-    const Tp* xs = (const Tp*)&x;
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[j] += load_as_f32<E>(xs + j);
+    for (int j = 0; j < V; ++j) acc[j] += load_as_f32<E>((const Tp*)&xs + j);
   }
-  for (int k = 0; k < K; ++k) {
-    const u32x4 x = *(const u32x4*)(Y + ((size_t)t * K + k) * d + col);
-    const Tp* xs = (const Tp*)&x;
+  for (int k0 = 0; k0 < K; k0 += G) {
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[j] += load_as_f32<E>(xs + j);
+    for (int i = 0; i < G; ++i) {
+      if (k0 + i >= K) break;
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += load_as_f32<E>((const Tp*)&xy[i] + j);
+    }
+    if (k0 + G < K) {  // the next group
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        if (k0 + G + i < K) xy[i] = *(const u32x4*)(yr + (size_t)(k0 + G + i) * d);
+    }
   }
   u32x4 out;
   Tp* os = (Tp*)&out;

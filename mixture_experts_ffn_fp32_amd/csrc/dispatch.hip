@@ -28,6 +28,26 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
+// Expert ids of token t's K pairs, all requested before any is used (up to
+// kKReg of them in registers; more are read again where needed).
+constexpr int kKReg = 16;
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int t, int K,
+                                         int (&ev)[kKReg]) {
+#pragma unroll
+  for (int k = 0; k < kKReg; ++k)
+    if (k < K) ev[k] = idx[(size_t)t * K + k];
+}
+// f(k, e) for each of token t's pairs in order k = 0 .. K-1 (register
+// indices fixed at compile time, so the ids stay in registers).
+template <class F>
+__device__ __forceinline__ void for_ids(const int32_t* __restrict__ idx, int t, int K,
+                                        const int (&ev)[kKReg], F f) {
+#pragma unroll
+  for (int k = 0; k < kKReg; ++k)
+    if (k < K) f(k, ev[k]);
+  for (int k = kKReg; k < K; ++k) f(k, idx[(size_t)t * K + k]);
+}
+
 // One wavefront per tile of 64 tokens; lane = token.
 __global__ __launch_bounds__(64) void tile_rank_kernel(const int32_t* __restrict__ idx, int T,
                                                        int N, int K,
@@ -40,19 +60,19 @@ __global__ __launch_bounds__(64) void tile_rank_kernel(const int32_t* __restrict
   for (int e = lane; e < N; e += 64) mask[e] = 0ull;
   __syncthreads();
   const unsigned long long bit = 1ull << lane;
+  int ev[kKReg];
+  if (t < T) load_ids(idx, t, K, ev);
   // ids outside [0, N) are ignored (the router never produces them)
   if (t < T)
-    for (int k = 0; k < K; ++k) {
-      const int e = idx[(size_t)t * K + k];
+    for_ids(idx, t, K, ev, [&](int, int e) {
       if ((unsigned)e < (unsigned)N) atomicOr(&mask[e], bit);
-    }
+    });
   __syncthreads();
   if (t < T) {
     const unsigned long long below = bit - 1ull;
-    for (int k = 0; k < K; ++k) {
-      const int e = idx[(size_t)t * K + k];
+    for_ids(idx, t, K, ev, [&](int k, int e) {
       rank[(size_t)t * K + k] = ((unsigned)e < (unsigned)N) ? __popcll(mask[e] & below) : 0;
-    }
+    });
   }
   for (int e = lane; e < N; e += 64) tile_counts[(size_t)tile * N + e] = __popcll(mask[e]);
 }
@@ -74,9 +94,17 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   const int C = (ntiles + G - 1) / G;
   const int lo = min(g * C, ntiles), hi = min(lo + C, ntiles);
 
+  // the chunk's counts, eight requested at a time before any is added
+  constexpr int B = 8;
   int s = 0;
   if (e < N)
-    for (int tl = lo; tl < hi; ++tl) s += tile_counts[(size_t)tl * N + e];
+    for (int t0 = lo; t0 < hi; t0 += B) {
+      int c[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) c[i] = t0 + i < hi ? tile_counts[(size_t)(t0 + i) * N + e] : 0;
+#pragma unroll
+      for (int i = 0; i < B; ++i) s += c[i];
+    }
   csum[tid] = s;
   __syncthreads();
   // per-expert exclusive scan over the G chunks, and the expert totals
@@ -110,9 +138,16 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   if (tid < 64 && tt.tiles1 != nullptr) tile_tables_wave(s_off, N, s_off[N], tt);
   if (e < N) {
     int run = s_off[e] + csum[tid];
-    for (int tl = lo; tl < hi; ++tl) {
-      tile_base[(size_t)tl * N + e] = run;
-      run += tile_counts[(size_t)tl * N + e];
+    for (int t0 = lo; t0 < hi; t0 += B) {
+      int c[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) c[i] = t0 + i < hi ? tile_counts[(size_t)(t0 + i) * N + e] : 0;
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        if (t0 + i < hi) {
+          tile_base[(size_t)(t0 + i) * N + e] = run;
+          run += c[i];
+        }
     }
   }
 }
@@ -145,11 +180,12 @@ __global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __res
   for (int e = lane; e < N; e += 64) mask[e] = 0ull;
   __syncthreads();
   const unsigned long long bit = 1ull << lane;
+  int ev[kKReg];
+  if (lane < T) load_ids(idx, lane, K, ev);
   if (lane < T)
-    for (int k = 0; k < K; ++k) {
-      const int e = idx[(size_t)lane * K + k];
+    for_ids(idx, lane, K, ev, [&](int, int e) {
       if ((unsigned)e < (unsigned)N) atomicOr(&mask[e], bit);
-    }
+    });
   __syncthreads();
   int carry = 0;
   for (int b = 0; b < N; b += 64) {
@@ -171,11 +207,10 @@ __global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __res
   if (tt.tiles1 != nullptr) tile_tables_wave(s_off, N, carry, tt);
   if (lane < T) {
     const unsigned long long below = bit - 1ull;
-    for (int k = 0; k < K; ++k) {
-      const int e = idx[(size_t)lane * K + k];
+    for_ids(idx, lane, K, ev, [&](int k, int e) {
       if ((unsigned)e < (unsigned)N)
         sorted_pair[s_off[e] + __popcll(mask[e] & below)] = lane * K + k;
-    }
+    });
   }
 }
 

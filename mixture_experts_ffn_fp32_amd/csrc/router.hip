@@ -105,10 +105,15 @@ __global__ __launch_bounds__(256) void router_kernel(const typename E::T* __rest
     rowp[i] = r < TB ? u + (size_t)min(t0 + r, T - 1) * d
                      : Eg + (size_t)min(r - TB, N - 1) * d;
   }
+  // the stages are taken in an order rotated per block (stage s reads
+  // contraction slice (s + rot) mod nsteps): every block reads all of E_gate,
+  // and all of them on the same lines at once would queue at one L2 channel
+  const int rot = (int)(blockIdx.x % (unsigned)nsteps);
   u32x4 stage[P][PASSES];
   auto issue = [&](int s, u32x4 (&st)[PASSES]) {
+    const int sr = s + rot < nsteps ? s + rot : s + rot - nsteps;
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) st[i] = *(const u32x4*)(rowp[i] + (size_t)s * kStep + c * E::kPerChunk);
+    for (int i = 0; i < PASSES; ++i) st[i] = *(const u32x4*)(rowp[i] + (size_t)sr * kStep + c * E::kPerChunk);
   };
   f32x4 acc[FW];
 #pragma unroll
@@ -268,7 +273,12 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
     float part[64];
 #pragma unroll
     for (int i = 0; i < 64; ++i) part[i] = 0.f;
-    for (int c = tid; c < nch; c += 256) {
+    for (int ci = tid; ci < nch; ci += 256) {
+      // chunk order rotated per block: the blocks read E_gate at the same
+      // time, and the same lines in the same order would queue at one L2
+      // channel after another
+      int c = ci + (int)((blockIdx.x * 8u) % (unsigned)nch);
+      if (c >= nch) c -= nch;
       float x[PC];
       u32x4 xw;  // the token chunk's raw words (bf16: four bf16 pairs)
       // 32 expert chunks in flight per batch
