@@ -5,12 +5,13 @@
 // largest s of each token are kept as its gates, the rest are zero.  Ties
 // are broken towards the lower expert index so that exactly K are kept.
 //
-// Layout of the work: one block = 32 tokens x all experts, 4 wavefronts
-// (two token groups x two expert halves), several stages of the token and
-// expert rows in flight (see router_kernel); batches of at most 128 tokens
-// take a one-block-per-token kernel (router_small_kernel).
+// Layout of the work: one block = 32 tokens x all experts, 4 computing
+// wavefronts (two token groups x two expert halves) fed by 4 loading
+// wavefronts through an LDS ring (see router_kernel); batches of at most 128
+// tokens take a one-block-per-token kernel (router_small_kernel).
 #include <cstdlib>
 
+#include "lds_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -58,112 +59,143 @@ __device__ __forceinline__ int router_lds_offset(int r, int c) {
   return r * (CH * 16) + ((c ^ (r & 15)) << 4);
 }
 
-// One block = 32 tokens x all experts (padded to NP = 16F, F even), four
-// wavefronts: wavefront w multiplies token group w & 1 (16 tokens) against
-// expert half w >> 1 (F / 2 fragments of 16), 16x16x32 bf16 MFMAs (16x16x4
-// for float32) with float32 accumulation.  A stage is CH 16-byte chunks of
-// every token row and expert row; the loads of P stages are in flight at
-// once in registers (each thread moves PASSES chunks per stage), and a stage
-// is written to one of two LDS buffers just before it is multiplied, so the
-// block is bound by the rate it reads u and E_gate rather than by one memory
-// round trip per stage.  After the last stage every wavefront writes its
-// logits to LDS and each 16-lane row group takes one token at a time for the
+// One block = 32 tokens x all experts (padded to NP = 16F, F even), eight
+// wavefronts.  Wavefronts 4-7 only load: a stage is CH 16-byte chunks of
+// every token row and expert row, brought into an S-slot LDS ring by
+// direct-to-LDS buffer loads (S - 1 stages in flight; the loaders wait for
+// the oldest with an exact vmcnt and release it with a barrier).
+// Wavefronts 0-3 only compute: wavefront w multiplies token group w & 1 (16
+// tokens) against expert half w >> 1 (F / 2 fragments of 16), 16x16x32 bf16
+// MFMAs (16x16x4 for float32) with float32 accumulation.  (With every
+// wavefront both loading and reading, the compiler cannot tell a ring slot's
+// reads from the other slots' loads and waits for all loads before reading.)
+// After the last stage the computing wavefronts write their logits to LDS and
+// each 16-lane row group of all eight wavefronts takes one token for the
 // softmax and top-K: 4-step DPP butterflies inside the row group.
 constexpr int kRouterTB = 32;
 
 template <class E, int F, int CH>
-__global__ __launch_bounds__(256) void router_kernel(const typename E::T* __restrict__ u,
+struct RouterCfg {
+  static constexpr int NP = 16 * F;                     // experts, padded
+  static constexpr int ROWS = kRouterTB + NP;           // rows per stage: tokens, then experts
+  static constexpr int RPI = 64 / CH;                   // rows per load instruction (1 KB)
+  static constexpr int NI = ROWS / (4 * RPI);           // loads per loading wavefront per stage
+  static constexpr int SLOT = ROWS * CH * 16;           // bytes per ring slot
+  static constexpr int S = 4 * SLOT <= 144 * 1024 ? 4 : 3;  // ring slots
+  static_assert(ROWS % (4 * RPI) == 0 && kRouterTB % RPI == 0, "stage shape");
+  static_assert(S * SLOT <= 144 * 1024 && (S - 2) * NI < 64, "ring");
+};
+
+template <class E, int F, int CH>
+__global__ __launch_bounds__(512) void router_kernel(const typename E::T* __restrict__ u,
                                                      const typename E::T* __restrict__ Eg,
                                                      const float* __restrict__ bias, int T, int d,
                                                      int N, int K, int32_t* __restrict__ idx,
                                                      float* __restrict__ gate,
                                                      float* __restrict__ scores) {
   using Tp = typename E::T;
-  constexpr int TB = kRouterTB;
-  constexpr int NP = 16 * F;            // experts, padded
-  constexpr int FW = F / 2;             // expert fragments per wavefront
-  constexpr int ROWS = TB + NP;         // rows per stage: tokens, then experts
-  constexpr int RPP = 256 / CH;         // rows covered by one pass of the block
-  constexpr int PASSES = ROWS / RPP;    // 16-byte loads per thread per stage
-  constexpr int P = PASSES * 4 <= 40 ? 4 : PASSES * 3 <= 40 ? 3 : PASSES * 2 <= 40 ? 2 : 1;
-  static_assert(F % 2 == 0 && ROWS % RPP == 0, "stage shape");
+  using C = RouterCfg<E, F, CH>;
+  constexpr int TB = kRouterTB, NP = C::NP, FW = F / 2, NI = C::NI, S = C::S;
+  constexpr int SLOT = C::SLOT;
   constexpr int kStep = CH * E::kPerChunk;  // contraction elements per stage
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][ROWS * CH * 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SLOT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
-  const int tg = wave & 1, fh = wave >> 1;
   const int nsteps = d / kStep;
-
-  // each thread moves chunk c of rows tid / CH + RPP * i; rows past T or N
-  // are clamped to a valid row (their results are never written)
-  const int c = tid % CH;
-  const Tp* rowp[PASSES];
-#pragma unroll
-  for (int i = 0; i < PASSES; ++i) {
-    const int r = tid / CH + RPP * i;
-    rowp[i] = r < TB ? u + (size_t)min(t0 + r, T - 1) * d
-                     : Eg + (size_t)min(r - TB, N - 1) * d;
-  }
-  // the stages are taken in an order rotated per block (stage s reads
-  // contraction slice (s + rot) mod nsteps): every block reads all of E_gate,
+  // the stages are taken in an order rotated per block (stage g reads
+  // contraction slice (g + rot) mod nsteps): every block reads all of E_gate,
   // and all of them on the same lines at once would queue at one L2 channel
   const int rot = (int)(blockIdx.x % (unsigned)nsteps);
-  u32x4 stage[P][PASSES];
-  auto issue = [&](int s, u32x4 (&st)[PASSES]) {
-    const int sr = s + rot < nsteps ? s + rot : s + rot - nsteps;
+  const size_t row_bytes = (size_t)d * sizeof(Tp);
+
+  if (wave >= 4) {
+    // ---- loading wavefronts: wavefront 4 + w moves rows (w NI + i) RPI ..
+    // + RPI - 1 of each stage with load i; lane L lands at LDS chunk
+    // position L % CH of row L / CH of that group and fetches the chunk the
+    // swizzle puts there.  Rows past T or N reread a valid row (never used).
+    const int w = wave - 4;
+    const uint8_t* base[NI];
+    uint32_t off[NI];
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) st[i] = *(const u32x4*)(rowp[i] + (size_t)sr * kStep + c * E::kPerChunk);
-  };
+    for (int i = 0; i < NI; ++i) {
+      const int r0 = (w * NI + i) * C::RPI, r = r0 + lane / CH, pos = lane % CH;
+      const int c = CH == 8 ? pos ^ ((r >> 1) & 7) : pos ^ (r & 15);
+      if (r0 < TB) {
+        base[i] = (const uint8_t*)(u + (size_t)t0 * d);
+        off[i] = (uint32_t)((size_t)(min(t0 + r, T - 1) - t0) * row_bytes) + c * 16;
+      } else {
+        base[i] = (const uint8_t*)Eg;
+        off[i] = (uint32_t)((size_t)min(r - TB, N - 1) * row_bytes) + c * 16;
+      }
+    }
+    auto issue = [&](int g) __attribute__((always_inline)) {
+      const int sr = g + rot < nsteps ? g + rot : g + rot - nsteps;
+      uint8_t* wr = ring + (g % S) * SLOT;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        dma16(uni(base[i] + (size_t)sr * CH * 16), off[i],
+              wr + ((w * NI + i) * C::RPI) * CH * 16);
+    };
+#pragma unroll
+    for (int j = 0; j < S - 1; ++j)
+      if (j < nsteps) issue(j);
+    for (int g = 0; g < nsteps; ++g) {
+      // stage g has landed: the stages after it in flight may stay
+      if (g + S - 2 < nsteps) MOE_WAIT_VMCNT((S - 2) * NI);
+      else MOE_WAIT_VMCNT(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // into the slot read at stage g - 1 (released by this barrier)
+      if (g + S - 1 < nsteps) issue(g + S - 1);
+    }
+  }
+
+  // ---- computing wavefronts
+  const int tg = wave & 1, fh = (wave >> 1) & 1;
   f32x4 acc[FW];
 #pragma unroll
   for (int f = 0; f < FW; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  if (wave < 4)
+  for (int g = 0; g < nsteps; ++g) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint8_t* buf = ring + (g % S) * SLOT;
 #pragma unroll
-  for (int j = 0; j < P; ++j)
-    if (j < nsteps) issue(j, stage[j]);
-  for (int s0 = 0; s0 < nsteps; s0 += P) {
+    for (int kg = 0; kg < CH / 4; ++kg) {  // k-groups of 4 chunks
+      const int ch = kg * 4 + (lane >> 4);
+      const u32x4 av = *(const u32x4*)(buf + router_lds_offset<CH>(tg * 16 + (lane & 15), ch));
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int s = s0 + j;
-      if (s < nsteps) {
-        uint8_t* buf = lds[s & 1];
-#pragma unroll
-        for (int i = 0; i < PASSES; ++i)
-          *(u32x4*)(buf + router_lds_offset<CH>(tid / CH + RPP * i, c)) = stage[j][i];
-        if (s + P < nsteps) issue(s + P, stage[j]);
-        __syncthreads();
-#pragma unroll
-        for (int kg = 0; kg < CH / 4; ++kg) {  // k-groups of 4 chunks
-          const int ch = kg * 4 + (lane >> 4);
-          const u32x4 av = *(const u32x4*)(buf + router_lds_offset<CH>(tg * 16 + (lane & 15), ch));
-#pragma unroll
-          for (int f = 0; f < FW; ++f) {
-            const u32x4 bv =
-                *(const u32x4*)(buf + router_lds_offset<CH>(TB + (fh * FW + f) * 16 + (lane & 15), ch));
-            acc[f] = mfma16(E{}, av, bv, acc[f]);
-          }
-        }
+      for (int f = 0; f < FW; ++f) {
+        const u32x4 bv =
+            *(const u32x4*)(buf + router_lds_offset<CH>(TB + (fh * FW + f) * 16 + (lane & 15), ch));
+        acc[f] = mfma16(E{}, av, bv, acc[f]);
       }
     }
+    MOE_WAIT_LGKMCNT0();  // this slot's reads are done before the next barrier
   }
 
   // acc[f][r]: token tg*16 + 4*(lane/16) + r, expert (fh*FW + f)*16 + lane%16.
   constexpr int LP = NP + 1;  // padded logit row (floats)
-  static_assert(TB * LP * 4 <= (int)sizeof(lds), "logits fit the stage buffers");
-  float* lg = (float*)&lds[0][0];
-  __syncthreads();  // every wavefront's last reads of the stage buffers are done
+  static_assert(TB * LP * 4 <= S * SLOT, "logits fit the ring");
+  float* lg = (float*)ring;
+  __syncthreads();  // every wavefront's last reads of the ring are done
+  if (wave < 4) {
 #pragma unroll
-  for (int f = 0; f < FW; ++f)
+    for (int f = 0; f < FW; ++f)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      lg[(tg * 16 + 4 * (lane >> 4) + r) * LP + (fh * FW + f) * 16 + (lane & 15)] = acc[f][r];
+      for (int r = 0; r < 4; ++r)
+        lg[(tg * 16 + 4 * (lane >> 4) + r) * LP + (fh * FW + f) * 16 + (lane & 15)] = acc[f][r];
+  }
   __syncthreads();
-  // softmax and top-K: row group grp of wavefront w takes tokens 8w + 4q + grp
+  // softmax and top-K, all eight wavefronts: row group grp of wavefront w
+  // takes token 4w + grp
   const int grp = lane >> 4, col = lane & 15;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int tl = wave * 8 + q * 4 + grp;
+  {
+    const int tl = wave * 4 + grp;
     const int t = t0 + tl;
     float v[F];
     float m = -INFINITY;
@@ -386,11 +418,11 @@ template <class E, int F>
 hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int T, int d, int N,
                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
   using Tp = typename E::T;
-  const dim3 grid((T + kRouterTB - 1) / kRouterTB), block(256);
+  const dim3 grid((T + kRouterTB - 1) / kRouterTB), block(512);
   const Tp* up = (const Tp*)u;
   const Tp* ep = (const Tp*)Eg;
   const size_t row = (size_t)d * sizeof(Tp);
-  constexpr int CHW = F <= 4 ? 32 : F == 8 ? 16 : 8;  // chunks per stage the registers allow
+  constexpr int CHW = F <= 4 ? 32 : F == 8 ? 16 : 8;  // chunks per stage the LDS ring holds
   if (row % (CHW * 16) == 0)
     router_kernel<E, F, CHW><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
   else
