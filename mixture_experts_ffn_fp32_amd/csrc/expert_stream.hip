@@ -127,10 +127,33 @@ __global__ __launch_bounds__(kSlThreads, 1) void expert_stream_long_kernel(Exper
     n1 = nt;
   } else {
     const int P = G / S;
-    q0 = b / P;
-    q1 = b < S * P ? q0 + 1 : q0;
-    n0 = nt * (b % P) / P;
-    n1 = nt * (b % P + 1) / P;
+    // A shared expert's M segments (its token rows in 16-row groups) stream
+    // the same weights.  The blocks of one share of its weight-row groups
+    // are placed 8 ids apart (workgroups are dealt round-robin over the 8
+    // XCDs), so all M sit on one XCD, start together and read the same rows
+    // in the same order: HBM serves the rows once and that XCD's L2 the
+    // other M - 1 times.  Groups of 8 such block sets fill windows of 8 M
+    // ids after the routed segments' blocks.
+    const int Sr = s_tab[V - (MODE == 1 ? a.K_s : (a.K_s > 0 ? 1 : 0))];  // routed segments
+    const int nsh = MODE == 1 ? a.K_s : (a.K_s > 0 ? 1 : 0);             // shared experts
+    const int M = nsh > 0 ? (S - Sr) / nsh : 0;  // segments per shared expert
+    const int base = Sr * P;
+    const int need = M > 0 ? ((nsh * P + 7) / 8) * 8 * M : 0;
+    int part = b % P;
+    if (b < base || M == 0 || base + need > G) {
+      q0 = b / P;
+      q1 = b < S * P ? q0 + 1 : q0;
+    } else {
+      const int r = b - base, win = 8 * M;
+      const int set = (r / win) * 8 + r % 8;  // block set: (shared expert, share)
+      const int m = (r % win) / 8;
+      const int e = set / P;
+      part = set % P;
+      q0 = Sr + e * M + m;
+      q1 = e < nsh ? q0 + 1 : q0;
+    }
+    n0 = nt * part / P;
+    n1 = nt * (part + 1) / P;
   }
   if (q0 >= q1 || n0 >= n1) return;  // whole block: no barrier is left behind
 
