@@ -282,16 +282,16 @@ def backward_only(args):
                       "tflops": round(fl / (ms / 1e3) / 1e12, 2)}), flush=True)
 
 
-def traffic_record(kernel_src: str, key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source (else None)."""
+def traffic_record(key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (profiles/traffic.json),
+    if it was taken on the current source of the kernel it names (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(key)
     if not rec:
         return None
-    src = open(kernel_src, "rb").read()
+    src = open(os.path.join(ROOT, "mixture_experts_ffn_fp32_amd", "csrc", rec["source"]), "rb").read()
     if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
         return None
     return rec.get("bytes_per_launch")
@@ -362,10 +362,9 @@ def main():
     g1_flops = 4.0 * w.d * w.I * w.T * (w.K + w.K_s)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     g1_tflops = g1_flops / (g1_ms / g1_n / 1e3) / 1e12
-    gemm1_src = os.path.join(ROOT, "mixture_experts_ffn_fp32_amd", "csrc", "expert_gemm.hip")
     roofline = {"bound": "mfma", "kernel": "expert_gemm1_swiglu", "achieved": round(g1_tflops, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(g1_tflops / peak, 4),
-                "traffic": traffic_record(gemm1_src, f"{w.name}:expert_gemm1_swiglu"),
+                "traffic": traffic_record(f"{w.name}:expert_gemm1_swiglu"),
                 "launch_ms": round(g1_ms / g1_n, 4),
                 "algorithmic_flops_per_launch": g1_flops}
     stage_ms = {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items()}
@@ -400,6 +399,10 @@ def main():
                   "experts_hit": hit,
                   "algorithmic_bytes": dbytes, "hbm_GBs": round(dbytes / dstep / 1e9, 1),
                   "hbm_frac": round(dbytes / dstep / 1e9 / PEAK_HBM_GBS, 4),
+                  # counter-measured HBM bytes of the two expert GEMMs (rocprofv3 FETCH_SIZE +
+                  # WRITE_SIZE, profiles/traffic.json; null once their source has changed)
+                  "gemm_traffic": {k: traffic_record(f"{dw.name}:{k}")
+                                   for k in ("expert_gemm1_swiglu", "expert_gemm2_down")},
                   "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in dstages.items()
                                if v[1]}}
         del dt_
