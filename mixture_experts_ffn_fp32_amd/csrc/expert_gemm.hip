@@ -344,9 +344,9 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(ExpertArgs a) {
 // slot after its last reads with its own waits and barrier).
 template <int NINST>
 __device__ __forceinline__ void dma_fill(uint8_t* __restrict__ wr, const uint8_t* base,
-                                         const uint32_t (&off)[NINST]) {
+                                         const uint32_t (&off)[NINST], int nrec = 0x7fffffff) {
 #pragma unroll
-  for (int i = 0; i < NINST; ++i) dma16(base, off[i], wr + i * 1024);
+  for (int i = 0; i < NINST; ++i) dma16(base, off[i], wr + i * 1024, nrec);
 }
 
 template <int FM, int FN, int RB, int BM, int BNB, int MODE>
@@ -466,16 +466,20 @@ constexpr int kDmaGroups = 2;
 // of group g, so neither the LDS latency nor a burst of loads holds the
 // MFMAs back.  A wavefront whose rows are all padding (`active` false) only
 // issues its loads.
-template <class E, int MODE, int FM, int NI>
+// kIssue false: the loads were issued already (nothing is issued here).
+template <class E, int MODE, int FM, int NI, bool kIssue = true>
 __device__ __forceinline__ void pipe_mma(const uint8_t* __restrict__ rd, int wm, int wn, int lane,
                                          f32x16 (&acc)[FM][4], bool active,
                                          const uint8_t* db, const uint32_t (&off)[NI],
                                          uint8_t* __restrict__ wr, int nrec = 0x7fffffff) {
-  constexpr int FN = 4, KG = kPipeRB / 32, PARTS = kDmaGroups, PER = NI / PARTS;
-  static_assert(NI % PARTS == 0 && PARTS <= KG, "DMA parts");
+  constexpr int FN = 4, KG = kPipeRB / 32, PARTS = kIssue ? kDmaGroups : 0,
+                PER = kIssue ? NI / kDmaGroups : 0;
+  static_assert(!kIssue || (NI % kDmaGroups == 0 && kDmaGroups <= KG), "DMA parts");
   if (!active) {
+    if (kIssue) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(db, off[i], wr + i * 1024, nrec);
+      for (int i = 0; i < NI; ++i) dma16(db, off[i], wr + i * 1024, nrec);
+    }
     return;
   }
   u32x4 af[2][FM], bfr[2][FN];
@@ -746,20 +750,24 @@ __global__ __launch_bounds__(64 * W, 1) void expert_gemm_pipe_kernel(ExpertArgs 
       if (s + 2 >= nsteps && tid == 0) s_claim = claim;
       // even k-step: slot 0 holds k-step s; k-step s + 1 goes to slot 1
       pipe_sync();
+      const uint8_t* db1 = pipe_dma_base<E, MODE>(a, ti, ld, s + 1 < nreal ? s + 1 : 0, is_a);
+      const int nrec1 = s + 1 < nreal ? 0x7fffffff : 0;
+      uint8_t* const wr1 = lds1 + wave * NINST * 1024;
+      // the next k-step's loads go out first (ahead of the previous tile's
+      // stores after a tile change, so they do not queue behind them)
+      dma_fill<NINST>(wr1, db1, ld.off, nrec1);
+      if (kDirect && s == 0 && pending) {  // the previous tile's results
+        pipe_store_direct<MODE, FM>(a, tp, wm, wn, acc, dst, gate);
+        zero_acc();
+      }
       if (s == 0) {
-        if (kDirect && pending) {  // the previous tile's results
-          pipe_store_direct<MODE, FM>(a, tp, wm, wn, acc, dst, gate);
-          zero_acc();
-        }
         // this tile's rows (GEMM2: the pair index now, its gate after the
         // next barrier, which awaits the lookup with the k-step's loads)
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) dst[fm] = pipe_row_dest<MODE>(a, ti, (wm * FM + fm) * 32 + (lane & 31));
         if (!kDirect) zero_acc();
       }
-      pipe_mma<E, MODE, FM>(lds0, wm, wn, lane, acc, active,
-                            pipe_dma_base<E, MODE>(a, ti, ld, s + 1 < nreal ? s + 1 : 0, is_a),
-                            ld.off, lds1 + wave * NINST * 1024, s + 1 < nreal ? 0x7fffffff : 0);
+      pipe_mma<E, MODE, FM, NINST, false>(lds0, wm, wn, lane, acc, active, db1, ld.off, wr1, nrec1);
       if (s == 0 && nsteps > 2 && tid == 0) reply = claim_issue(ctr + x);
       // odd k-step: slot 1 holds k-step s + 1; slot 0 gets k-step s + 2, or
       // the next tile's first k-step after the last one
