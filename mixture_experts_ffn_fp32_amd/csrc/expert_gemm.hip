@@ -371,9 +371,12 @@ __device__ __forceinline__ void load_frags(const uint8_t* __restrict__ rd, int k
 // 16 bytes at the wavefront's LDS address + 16 L), one 128-byte k-step per
 // row, in a two-slot ring: k-step s + 1 lands while k-step s is multiplied.
 // The LDS swizzle is applied on the global side (lane L fetches the chunk that
-// belongs in LDS slot L).  The kernel is persistent; while a tile's results
-// are written out (staged through the free ring slot as bf16 rows), the next
-// tile's first k-step is already loading.  One block per CU.
+// belongs in LDS slot L).  The kernel is persistent and the next tile's
+// first k-step loads during a tile's last one.  bf16 results leave straight
+// from the accumulators (16-byte runs after lane exchanges) once the next
+// tile's first k-step has landed and its second k-step's loads are issued;
+// float32 results are written at the end of their tile (store_tile).  One
+// block per CU.
 constexpr int kPipeBM = 256, kPipeBNB = 256, kPipeRB = 128;
 constexpr int kPipeSlot = (kPipeBM + kPipeBNB) * kPipeRB;  // 64 KB
 template <int W>
