@@ -28,15 +28,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const typename E::T* __res
   const int col = (int)(chunk % cpr) * V;
 
   // every row of the token is requested before any is added (in groups of
-  // eight Y rows; the sum keeps the fixed order u, Y_shared, Y_0 .. Y_{K-1})
+  // eight Y rows; the sum keeps the fixed order u, Y_shared, Y_0 .. Y_{K-1}).
+  // The inputs are read once here: non-temporal loads, so they do not push
+  // other data out of the caches.
   constexpr int G = 8;
   const Tp* yr = Y + (size_t)t * K * d + col;
-  u32x4 xu = *(const u32x4*)(u + (size_t)t * d + col);
-  u32x4 xs = Ys != nullptr ? *(const u32x4*)(Ys + (size_t)t * d + col) : u32x4{0u, 0u, 0u, 0u};
+  u32x4 xu = __builtin_nontemporal_load((const u32x4*)(u + (size_t)t * d + col));
+  u32x4 xs = Ys != nullptr ? __builtin_nontemporal_load((const u32x4*)(Ys + (size_t)t * d + col))
+                           : u32x4{0u, 0u, 0u, 0u};
   u32x4 xy[G];
 #pragma unroll
   for (int j = 0; j < G; ++j)
-    if (j < K) xy[j] = *(const u32x4*)(yr + (size_t)j * d);
+    if (j < K) xy[j] = __builtin_nontemporal_load((const u32x4*)(yr + (size_t)j * d));
   float acc[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) acc[j] = load_as_f32<E>((const Tp*)&xu + j);
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const typename E::T* __res
     if (k0 + G < K) {  // the next group
 #pragma unroll
       for (int i = 0; i < G; ++i)
-        if (k0 + G + i < K) xy[i] = *(const u32x4*)(yr + (size_t)(k0 + G + i) * d);
+        if (k0 + G + i < K) xy[i] = __builtin_nontemporal_load((const u32x4*)(yr + (size_t)(k0 + G + i) * d));
     }
   }
   u32x4 out;
