@@ -271,7 +271,8 @@ __global__ __launch_bounds__(512) void router_kernel(const typename E::T* __rest
 // in the same order, so all hold the same maximum and sum; an expert's place
 // in the top-K is its rank, the number of experts with a larger score or an
 // equal score and a smaller index (the same choice as K rounds of argmax with
-// the lowest index winning ties).
+// the lowest index winning ties).  With at most 64 experts one wavefront
+// does all of it, lane e holding expert e (maximum and sum by butterflies).
 constexpr int kSmallRouterMaxT = 128;
 
 // Element q of a 16-byte chunk as float32.
@@ -381,6 +382,35 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
           (((s_red[0][lane] + s_red[1][lane]) + s_red[2][lane]) + s_red[3][lane]) +
           (bias ? bias[eb + lane] : 0.f);
     __syncthreads();
+  }
+  if (N <= 64) {
+    // one wavefront, lane e holding expert e: the maximum and the sum by xor
+    // butterflies (every lane ends with the same bits), the rank from the
+    // scores in LDS (same wavefront: its LDS write is seen by its next read)
+    if (wave != 0) return;
+    const bool live = lane < N;
+    const float z = live ? s_logit[lane] : -INFINITY;
+    float m = z;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float ex = live ? expf(z - m) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    const float sc = ex / sum;
+    s_p[lane] = live ? sc : -1.f;  // -1: below every score
+    if (live && scores != nullptr) scores[(size_t)t * N + lane] = sc;
+    int rank = 0;
+#pragma unroll 16
+    for (int e = 0; e < 64; ++e) {
+      const float o = s_p[e];
+      rank += (o > sc || (o == sc && e < lane)) ? 1 : 0;
+    }
+    if (live && rank < K) {
+      idx[(size_t)t * K + rank] = lane;
+      gate[(size_t)t * K + rank] = sc;
+    }
+    return;
   }
   // softmax: the maximum and the sum in expert order, the same in every thread
   float m = -INFINITY;
