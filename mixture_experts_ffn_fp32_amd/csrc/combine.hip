@@ -74,9 +74,8 @@ hipError_t launch_t(const void* u, const void* Y, const void* Ys, int T, int d, 
   const long long chunks = (long long)T * (d / E::kPerChunk);
   const long long blocks = (chunks + 255) / 256;
   if (blocks <= 0) return hipSuccess;
-  combine_kernel<E><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
-      (const Tp*)u, (const Tp*)Y, (const Tp*)Ys, T, d, K, (Tp*)h);
-  return hipGetLastError();
+  return launch_kernel(combine_kernel<E>, dim3((unsigned)blocks), dim3(256), st, (const Tp*)u,
+                       (const Tp*)Y, (const Tp*)Ys, T, d, K, (Tp*)h);
 }
 
 }  // namespace

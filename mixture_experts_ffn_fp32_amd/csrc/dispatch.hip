@@ -219,15 +219,15 @@ __global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __res
 hipError_t launch_dispatch_small(const int32_t* idx, int T, int N, int K, int32_t* counts,
                                  int32_t* offsets, int32_t* sorted_pair, const TileTableOut& tt,
                                  hipStream_t stream) {
-  dispatch_small_kernel<<<1, 64, 0, stream>>>(idx, T, N, K, counts, offsets, sorted_pair, tt);
-  return hipGetLastError();
+  return launch_kernel(dispatch_small_kernel, dim3(1), dim3(64), stream, idx, T, N, K, counts,
+                       offsets, sorted_pair, tt);
 }
 
 hipError_t launch_tile_rank(const int32_t* idx, int T, int N, int K, int32_t* tile_counts,
                             int32_t* rank, hipStream_t stream) {
   const int ntiles = (T + kRankTile - 1) / kRankTile;
-  tile_rank_kernel<<<ntiles, 64, 0, stream>>>(idx, T, N, K, tile_counts, rank);
-  return hipGetLastError();
+  return launch_kernel(tile_rank_kernel, dim3(ntiles), dim3(64), stream, idx, T, N, K,
+                       tile_counts, rank);
 }
 
 hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, int32_t* counts,
@@ -235,17 +235,16 @@ hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, i
                                 hipStream_t stream) {
   int np2 = 1;
   while (np2 < N) np2 <<= 1;
-  dispatch_scan_kernel<<<1, 1024, 0, stream>>>(tile_counts, ntiles, N, np2, counts, offsets,
-                                               tile_base, tt);
-  return hipGetLastError();
+  return launch_kernel(dispatch_scan_kernel, dim3(1), dim3(1024), stream, tile_counts, ntiles, N,
+                       np2, counts, offsets, tile_base, tt);
 }
 
 hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_base,
                           int T, int N, int K, int32_t* sorted_pair, hipStream_t stream) {
   const long long pairs = (long long)T * K;
   const int blocks = (int)((pairs + 255) / 256);
-  scatter_kernel<<<blocks, 256, 0, stream>>>(idx, rank, tile_base, T, N, K, sorted_pair);
-  return hipGetLastError();
+  return launch_kernel(scatter_kernel, dim3(blocks), dim3(256), stream, idx, rank, tile_base, T, N,
+                       K, sorted_pair);
 }
 
 }  // namespace moe

@@ -1096,8 +1096,8 @@ hipError_t launch_reg(const ExpertArgs& a, hipStream_t st) {
   const long long g = grid_tiles(a, BM, (MODE == 1 ? a.I : a.d) / BNO, MODE);
   if (g <= 0) return hipSuccess;
   if (g > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  expert_gemm_kernel<E, WM, WN, FM, FN, MODE><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
-  return hipGetLastError();
+  return launch_kernel(expert_gemm_kernel<E, WM, WN, FM, FN, MODE>, dim3((unsigned)g), dim3(256),
+                       st, a);
 }
 
 // Compute units of the current device (cached per device).
@@ -1120,8 +1120,8 @@ hipError_t launch_pipe(const ExpertArgs& a, hipStream_t st) {
   long long g = grid_tiles(a, kPipeBM, ((MODE == 1 ? a.I : a.d) + BNO - 1) / BNO, MODE);
   if (g <= 0) return hipSuccess;
   g = std::min<long long>(g, (long long)cu_count());  // persistent: one block per CU
-  expert_gemm_pipe_kernel<E, MODE, W><<<dim3((unsigned)g), dim3(PipeCfg<W>::kThreads), 0, st>>>(a);
-  return hipGetLastError();
+  return launch_kernel(expert_gemm_pipe_kernel<E, MODE, W>, dim3((unsigned)g),
+                       dim3(PipeCfg<W>::kThreads), st, a);
 }
 
 template <int MODE>
@@ -1129,8 +1129,8 @@ hipError_t launch_stream(const ExpertArgs& a, hipStream_t st) {
   long long g = grid_tiles(a, kStrBM, str_nt<MODE>(a), MODE);
   if (g <= 0) return hipSuccess;
   g = std::min<long long>(g, (long long)cu_count());  // persistent: one block per CU
-  expert_gemm_stream_kernel<MODE><<<dim3((unsigned)g), dim3(kStrThreads), 0, st>>>(a);
-  return hipGetLastError();
+  return launch_kernel(expert_gemm_stream_kernel<MODE>, dim3((unsigned)g), dim3(kStrThreads), st,
+                       a);
 }
 
 template <class E, int MODE>
@@ -1164,9 +1164,8 @@ TileTableOut expert_tile_tables(int dtype, const ExpertArgs& a) {
 }
 
 hipError_t launch_tile_table(int dtype, const ExpertArgs& a, hipStream_t stream) {
-  tile_table_kernel<<<1, 64, 0, stream>>>(a.offsets, a.N, a.T * a.K,
-                                          expert_tile_tables(dtype, a));
-  return hipGetLastError();
+  return launch_kernel(tile_table_kernel, dim3(1), dim3(64), stream, a.offsets, a.N, a.T * a.K,
+                       expert_tile_tables(dtype, a));
 }
 
 hipError_t launch_gemm1(int dtype, const ExpertArgs& a, hipStream_t stream) {

@@ -394,10 +394,8 @@ hipError_t launch_stream_long(int mode, const ExpertArgs& a, int cus, hipStream_
   if (g <= 0) return hipSuccess;
   g = g < cus ? g : cus;  // persistent: one block per CU
   if (mode == 1)
-    expert_stream_long_kernel<1><<<dim3((unsigned)g), dim3(kSlThreads), 0, st>>>(a);
-  else
-    expert_stream_long_kernel<2><<<dim3((unsigned)g), dim3(kSlThreads), 0, st>>>(a);
-  return hipGetLastError();
+    return launch_kernel(expert_stream_long_kernel<1>, dim3((unsigned)g), dim3(kSlThreads), st, a);
+  return launch_kernel(expert_stream_long_kernel<2>, dim3((unsigned)g), dim3(kSlThreads), st, a);
 }
 
 }  // namespace moe

@@ -168,25 +168,44 @@ struct Timing {
 };
 Timing g_timing;
 
-// Records an event pair around one stage when timing is on.
-// Calls that must not allocate pass record = false (event creation allocates).
+// The stage being enqueued on this thread and its event pair (see
+// moe::stage_launch_events): the first launch of the stage carries the start
+// event, every launch the stop event.
+struct ScopeTiming {
+  bool active = false, launched = false;
+  hipEvent_t a = nullptr, b = nullptr;
+};
+thread_local ScopeTiming g_scope;
+
+// Times one stage when timing is on: the pair of events rides on the stage's
+// kernel launches.  Calls that must not allocate pass record = false (event
+// creation allocates).
 struct StageScope {
   int stage;
-  hipStream_t st;
-  hipEvent_t a = nullptr, b = nullptr;
-  StageScope(int s, hipStream_t stream, bool record = true) : stage(s), st(stream) {
+  bool mine = false;
+  StageScope(int s, hipStream_t, bool record = true) : stage(s) {
     if (!record) return;
     std::lock_guard<std::mutex> g(g_timing.mu);
     if (!g_timing.on || !((g_timing.mask >> s) & 1u)) return;
-    a = g_timing.get();
-    b = g_timing.get();
-    if (a && b) (void)hipEventRecord(a, st);
+    hipEvent_t a = g_timing.get(), b = g_timing.get();
+    if (!(a && b)) {
+      if (a) g_timing.pool.push_back(a);
+      if (b) g_timing.pool.push_back(b);
+      return;
+    }
+    g_scope = ScopeTiming{true, false, a, b};
+    mine = true;
   }
   ~StageScope() {
-    if (!(a && b)) return;
-    (void)hipEventRecord(b, st);
+    if (!mine) return;
     std::lock_guard<std::mutex> g(g_timing.mu);
-    g_timing.recs.push_back({stage, a, b});
+    if (g_scope.launched) {
+      g_timing.recs.push_back({stage, g_scope.a, g_scope.b});
+    } else {  // nothing was launched (an empty batch)
+      g_timing.pool.push_back(g_scope.a);
+      g_timing.pool.push_back(g_scope.b);
+    }
+    g_scope = ScopeTiming{};
   }
 };
 
@@ -415,6 +434,15 @@ hipError_t scratch_of_device(char** out) {
 }
 
 }  // namespace
+
+namespace moe {
+LaunchEvents stage_launch_events() {
+  if (!g_scope.active) return LaunchEvents{nullptr, nullptr};
+  const LaunchEvents ev{g_scope.launched ? nullptr : g_scope.a, g_scope.b};
+  g_scope.launched = true;
+  return ev;
+}
+}  // namespace moe
 
 extern "C" {
 

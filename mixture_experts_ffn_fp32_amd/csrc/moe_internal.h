@@ -1,10 +1,30 @@
 // Internal declarations shared by the gfx950 kernels and the C-ABI host code.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Timing of the stage being enqueued (the C ABI's stage scopes, when timing is
+// on): the next launch's start / stop events (null when the stage is not
+// timed; the start only on the stage's first launch, the stop on each, so the
+// pair spans all of the stage's kernels).  They ride on the kernel dispatch
+// itself (hipExtLaunchKernel), so timing puts no marker packets between
+// kernels.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+LaunchEvents stage_launch_events();
+
+template <class... P, class... A>
+inline hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st,
+                                A... args) {
+  const LaunchEvents ev = stage_launch_events();
+  hipExtLaunchKernelGGL(k, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- types
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));

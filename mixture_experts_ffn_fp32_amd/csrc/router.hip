@@ -454,10 +454,10 @@ hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int
   const size_t row = (size_t)d * sizeof(Tp);
   constexpr int CHW = F <= 4 ? 32 : F == 8 ? 16 : 8;  // chunks per stage the LDS ring holds
   if (row % (CHW * 16) == 0)
-    router_kernel<E, F, CHW><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  else
-    router_kernel<E, F, 8><<<grid, block, 0, st>>>(up, ep, bias, T, d, N, K, idx, gate, scores);
-  return hipGetLastError();
+    return launch_kernel(router_kernel<E, F, CHW>, grid, block, st, up, ep, bias, T, d, N, K, idx,
+                         gate, scores);
+  return launch_kernel(router_kernel<E, F, 8>, grid, block, st, up, ep, bias, T, d, N, K, idx, gate,
+                       scores);
 }
 
 // Batches of at most kSmallRouterMaxT tokens take the one-block-per-token
@@ -472,9 +472,8 @@ hipError_t launch_router_t(const void* u, const void* Eg, const float* bias, int
                            int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
   using Tp = typename E::T;
   if (T <= kSmallRouterMaxT && router_small()) {
-    router_small_kernel<E><<<T, 256, 0, st>>>((const Tp*)u, (const Tp*)Eg, bias, T, d, N, K, idx,
-                                              gate, scores);
-    return hipGetLastError();
+    return launch_kernel(router_small_kernel<E>, dim3(T), dim3(256), st, (const Tp*)u,
+                         (const Tp*)Eg, bias, T, d, N, K, idx, gate, scores);
   }
   if (N <= 32) return launch_router_f<E, 2>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
   if (N <= 64) return launch_router_f<E, 4>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);

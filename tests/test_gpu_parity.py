@@ -248,6 +248,44 @@ def test_layer_forward_short_run_streaming(name, monkeypatch):
             w.name)
 
 
+@pytest.mark.parametrize("name", ["pp_ragged_bf16", "decode_n256_bf16", "one_token_bf16"])
+def test_stage_timing_covers_every_launched_stage(name):
+    """Timing on: every stage the forward launches reports one launch per call with a
+    positive time (the events ride on the stage's kernel dispatches), stages limited by the
+    mask report nothing, and the output is the same bits as without timing."""
+    up = Uploaded(small_inputs(name))
+    w = up.w
+    say(f"stage timing {w.name}")
+    args = (up.u, up.E, up.W_routed, up.W_shared, w.N, w.K, w.K_s, up.bias)
+    h0 = mx.layer_forward(*args)
+    torch.cuda.synchronize()
+    mx.timing_read()
+    mx.timing_enable(True)
+    h1 = mx.layer_forward(*args)
+    h2 = mx.layer_forward(*args)
+    torch.cuda.synchronize()
+    mx.timing_enable(False)
+    st = mx.timing_read()
+    small_batch = w.T <= 64
+    expect = {"router", "expert_gemm1_swiglu", "expert_gemm2_down", "combine", "tile_rank"}
+    if not small_batch:
+        expect |= {"dispatch_scan", "scatter"}
+    for name_, (ms, n) in st.items():
+        if name_ in expect:
+            assert n == 2 and ms > 0, (name_, ms, n)
+        else:
+            assert n == 0, (name_, ms, n)
+    mx.timing_enable(True, ["expert_gemm1_swiglu"])
+    h3 = mx.layer_forward(*args)
+    torch.cuda.synchronize()
+    mx.timing_enable(False)
+    st = mx.timing_read()
+    assert st["expert_gemm1_swiglu"][1] == 1 and st["expert_gemm1_swiglu"][0] > 0
+    assert sum(n for k, (_, n) in st.items() if k != "expert_gemm1_swiglu") == 0
+    for hx in (h1, h2, h3):
+        assert torch.equal(hx, h0)
+
+
 def test_deterministic_and_chunk_invariant(small):
     w = small.w
     if w.T < 4:
