@@ -5,10 +5,12 @@
 // want each expert's tokens contiguous, so the pairs p = t*K + k are sorted
 // by expert, ascending p within an expert (a stable counting sort):
 //
-//  1. tile_rank: per 64-token tile, a 64-bit lane mask per expert in LDS
-//     gives each pair its rank among the tile's pairs of the same expert
-//     (popcount of the lower lanes) and each expert's count in the tile.
-//     Integer only, no global atomics, deterministic.
+//  1. tile_rank: per tile of kRankTile (32) tokens, a lane mask per expert
+//     in LDS gives each pair its rank among the tile's pairs of the same
+//     expert (popcount of the lower lanes) and each expert's count in the
+//     tile.  Integer only, no global atomics, deterministic.  The tiled
+//     router does the same for its 32-token blocks in its own epilogue, and
+//     the layer forward then skips this launch.
 //  2. dispatch_scan: one block turns tile counts into per-expert totals,
 //     offsets (exclusive scan over experts) and per-(tile, expert) bases.
 //  3. scatter: sorted_pair[base + rank] = p.
@@ -48,15 +50,17 @@ __device__ __forceinline__ void for_ids(const int32_t* __restrict__ idx, int t, 
   for (int k = kKReg; k < K; ++k) f(k, idx[(size_t)t * K + k]);
 }
 
-// One wavefront per tile of 64 tokens; lane = token.
+// One wavefront per tile of kRankTile tokens; lane = token (lanes past the
+// tile idle).
 __global__ __launch_bounds__(64) void tile_rank_kernel(const int32_t* __restrict__ idx, int T,
                                                        int N, int K,
                                                        int32_t* __restrict__ tile_counts,
                                                        int32_t* __restrict__ rank) {
   __shared__ unsigned long long mask[256];
+  static_assert(kRankTile <= 64, "one lane per token");
   const int lane = threadIdx.x;
   const int tile = blockIdx.x;
-  const int t = tile * kRankTile + lane;
+  const int t = lane < kRankTile ? tile * kRankTile + lane : T;
   for (int e = lane; e < N; e += 64) mask[e] = 0ull;
   __syncthreads();
   const unsigned long long bit = 1ull << lane;
@@ -74,61 +78,84 @@ __global__ __launch_bounds__(64) void tile_rank_kernel(const int32_t* __restrict
       rank[(size_t)t * K + k] = ((unsigned)e < (unsigned)N) ? __popcll(mask[e] & below) : 0;
     });
   }
-  for (int e = lane; e < N; e += 64) tile_counts[(size_t)tile * N + e] = __popcll(mask[e]);
+  const int row = rank_row((int)gridDim.x);
+  for (int e = lane; e < N; e += 64) tile_counts[(size_t)e * row + tile] = __popcll(mask[e]);
 }
 
-// One block of 1024 threads.  Thread (e, g) owns expert e and the contiguous
-// chunk g of the tiles; G = 1024 / NP2 chunks per expert (NP2 = N rounded up
-// to a power of two).
+// Inclusive scan over segments of G lanes (G a power of two, at most 64).
+__device__ __forceinline__ int seg_inclusive_scan(int x, int g, int G) {
+  for (int o = 1; o < G; o <<= 1) {
+    const int y = __shfl_up(x, o, G);
+    if (g >= o) x += y;
+  }
+  return x;
+}
+
+// One block of 1024 threads.  Expert e's row of tile counts is read in
+// rounds of G 16-byte groups (4 tiles each) by G consecutive lanes (G =
+// 1024 / NP2 capped at 64, NP2 = N rounded up to a power of two), so each
+// round is one coalesced run and its prefix a segmented lane scan; up to R
+// rounds stay in registers between the totals and the bases, longer rows
+// are read again.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ tile_counts,
                                                              int ntiles, int N, int NP2,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ tile_base,
                                                              TileTableOut tt) {
-  __shared__ int csum[1024];     // [g][e] chunk sums, later chunk bases
   __shared__ int s_off[257];
   const int tid = threadIdx.x;
-  const int e = tid % NP2, g = tid / NP2;
-  const int G = 1024 / NP2;
-  const int C = (ntiles + G - 1) / G;
-  const int lo = min(g * C, ntiles), hi = min(lo + C, ntiles);
+  const int G = min(1024 / NP2, 64);
+  const int g = tid % G, e = tid / G;
+  const bool live = e < N;
+  const int row = rank_row(ntiles), nq = row / 4;  // 16-byte groups per row
+  const int rounds = (nq + G - 1) / G;
+  const u32x4* src = (const u32x4*)(tile_counts + (size_t)(live ? e : 0) * row);
+  // group q of the row, the counts past the last tile (row padding) as 0
+  auto group = [&](int q) {
+    u32x4 v = q < nq ? src[q] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * q + j >= ntiles) v[j] = 0u;
+    return v;
+  };
+  auto sum4 = [](u32x4 v) { return (int)(v[0] + v[1] + v[2] + v[3]); };
 
-  // the chunk's counts, eight requested at a time before any is added
-  constexpr int B = 8;
+  constexpr int R = 16;
+  const bool in_regs = rounds <= R;
+  u32x4 cr[R];
   int s = 0;
-  if (e < N)
-    for (int t0 = lo; t0 < hi; t0 += B) {
-      int c[B];
+  if (live) {
+    if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < B; ++i) c[i] = t0 + i < hi ? tile_counts[(size_t)(t0 + i) * N + e] : 0;
+      for (int i = 0; i < R; ++i) cr[i] = i < rounds ? group(i * G + g) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < B; ++i) s += c[i];
-    }
-  csum[tid] = s;
-  __syncthreads();
-  // per-expert exclusive scan over the G chunks, and the expert totals
-  if (tid < NP2) {
-    int run = 0;
-    for (int gg = 0; gg < G; ++gg) {
-      const int v = csum[gg * NP2 + tid];
-      csum[gg * NP2 + tid] = run;
-      run += v;
-    }
-    if (tid < N) {
-      counts[tid] = run;
-      s_off[tid] = run;
+      for (int i = 0; i < R; ++i) s += sum4(cr[i]);
+    } else {
+      for (int i0 = 0; i0 < rounds; i0 += R) {
+        u32x4 c[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) c[i] = i0 + i < rounds ? group((i0 + i) * G + g) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < R; ++i) s += sum4(c[i]);
+      }
     }
   }
+  // the expert's total: the last lane of its segment
+  const int tot = __shfl(seg_inclusive_scan(s, g, G), G - 1, G);
+  if (live && g == 0) s_off[e] = tot;
   __syncthreads();
   // exclusive scan of the totals over experts (first wavefront, 64 at a time)
   if (tid < 64) {
     int carry = 0;
     for (int b = 0; b < N; b += 64) {
       const int v = (b + tid < N) ? s_off[b + tid] : 0;
-      const int inc = wave_inclusive_scan(v);
-      const int total = __shfl(inc, 63);
-      if (b + tid < N) s_off[b + tid] = carry + inc - v;
+      const int incv = wave_inclusive_scan(v);
+      const int total = __shfl(incv, 63);
+      if (b + tid < N) {
+        counts[b + tid] = v;
+        s_off[b + tid] = carry + incv - v;
+      }
       carry += total;
     }
     if (tid == 0) s_off[N] = carry;
@@ -136,19 +163,30 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   __syncthreads();
   for (int i = tid; i <= N; i += 1024) offsets[i] = s_off[i];
   if (tid < 64 && tt.tiles1 != nullptr) tile_tables_wave(s_off, N, s_off[N], tt);
-  if (e < N) {
-    int run = s_off[e] + csum[tid];
-    for (int t0 = lo; t0 < hi; t0 += B) {
-      int c[B];
+  // each tile's base: the expert's offset plus the counts of the row's
+  // earlier tiles, round by round (every lane of a segment takes part in
+  // each round's scan)
+  u32x4* dstb = (u32x4*)(tile_base + (size_t)(live ? e : 0) * row);
+  int run = live ? s_off[e] : 0;
+  auto round_bases = [&](int q, u32x4 c) {
+    const int gs = sum4(c);
+    const int inc = seg_inclusive_scan(gs, g, G);
+    uint32_t b = (uint32_t)(run + inc - gs);
+    u32x4 out;
 #pragma unroll
-      for (int i = 0; i < B; ++i) c[i] = t0 + i < hi ? tile_counts[(size_t)(t0 + i) * N + e] : 0;
-#pragma unroll
-      for (int i = 0; i < B; ++i)
-        if (t0 + i < hi) {
-          tile_base[(size_t)(t0 + i) * N + e] = run;
-          run += c[i];
-        }
+    for (int j = 0; j < 4; ++j) {
+      out[j] = b;
+      b += c[j];
     }
+    if (live && q < nq) dstb[q] = out;
+    run += __shfl(inc, G - 1, G);
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (i < rounds) round_bases(i * G + g, cr[i]);
+  } else {
+    for (int i = 0; i < rounds; ++i) round_bases(i * G + g, live ? group(i * G + g) : u32x4{0u, 0u, 0u, 0u});
   }
 }
 
@@ -162,7 +200,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int t = (int)(p / K);
   const int e = idx[p];
   if ((unsigned)e >= (unsigned)N) return;
-  sorted_pair[tile_base[(size_t)(t / kRankTile) * N + e] + rank[p]] = (int32_t)p;
+  const int row = rank_row((T + kRankTile - 1) / kRankTile);
+  sorted_pair[tile_base[(size_t)e * row + t / kRankTile] + rank[p]] = (int32_t)p;
 }
 
 // A batch of at most 64 tokens in one launch (one wavefront, lane = token):

@@ -117,7 +117,7 @@ Layout make_layout(int T, int d, int I, int N, int K, int K_s, int dtype) {
     return at;
   };
   const size_t TK = (size_t)T * K, es = elem_size(dtype);
-  const size_t nt = (size_t)rank_tiles(T);
+  const size_t nt = (size_t)moe::rank_row(rank_tiles(T));
   L.idx = take(TK * 4);
   L.gate = take(TK * 4);
   L.rank = take(TK * 4);
@@ -137,7 +137,7 @@ Layout make_layout(int T, int d, int I, int N, int K, int K_s, int dtype) {
 }
 
 size_t dispatch_ws_bytes(int T, int N, int K) {
-  const size_t nt = (size_t)rank_tiles(T);
+  const size_t nt = (size_t)moe::rank_row(rank_tiles(T));
   return align256((size_t)T * K * 4) + 2 * align256(nt * N * 4);
 }
 size_t expert_ws_bytes(int N, int K_s) {
@@ -255,17 +255,18 @@ hipError_t side_of_device(Side** out) {
 moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* rank,
                           int32_t* tile_counts, int32_t* tile_base, hipStream_t st,
-                          const moe::TileTableOut* tables = nullptr, bool rec = true) {
+                          const moe::TileTableOut* tables = nullptr, bool rec = true,
+                          bool ranked = false) {
   hipError_t e;
   const moe::TileTableOut tt = tables != nullptr ? *tables : moe::TileTableOut{};
-  if (T <= moe::kRankTile) {  // one tile: ranks, scan and scatter in one launch
+  if (T <= moe::kSmallDispatchT) {  // ranks, scan and scatter in one launch
     StageScope sc(1, st, rec);
     if ((e = moe::launch_dispatch_small(idx, T, N, K, counts, offsets, sorted_pair, tt, st)) !=
         hipSuccess)
       return hip_fail(e, "dispatch launch");
     return MOE_OK;
   }
-  {
+  if (!ranked) {  // (ranked: the router wrote them)
     StageScope sc(1, st, rec);
     if ((e = moe::launch_tile_rank(idx, T, N, K, tile_counts, rank, st)) != hipSuccess)
       return hip_fail(e, "tile rank launch");
@@ -381,16 +382,21 @@ moe_status_t forward_enqueue(const void* u, const void* E_gate, const void* W_ro
       return hip_fail(e, "shared-expert launches");
     ar.K_s = 0;
   }
+  // the tiled router also writes the dispatch ranks of large batches
+  bool ranked = false;
+  const bool want_ranks = T > moe::kSmallDispatchT;
   {
     StageScope sc(0, st, rec);
-    if ((e = moe::launch_router(dtype, u, E_gate, gate_bias, T, d, N, K, idx, gate, nullptr, st)) !=
-        hipSuccess)
+    if ((e = moe::launch_router(dtype, u, E_gate, gate_bias, T, d, N, K, idx, gate, nullptr, st,
+                                want_ranks ? (int32_t*)(ws + L.rank) : nullptr,
+                                want_ranks ? (int32_t*)(ws + L.tile_counts) : nullptr,
+                                &ranked)) != hipSuccess)
       return hip_fail(e, "router launch");
   }
   const moe::TileTableOut tables = moe::expert_tile_tables(dtype, ar);
   if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
                         (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
-                        (int32_t*)(ws + L.tile_base), st, &tables, rec)) != MOE_OK)
+                        (int32_t*)(ws + L.tile_base), st, &tables, rec, ranked)) != MOE_OK)
     return s;
   if ((s = run_experts(dtype, ar, st, true, rec)) != MOE_OK) return s;
   if (side && (e = hipStreamWaitEvent(st, sd->join, 0)) != hipSuccess)
@@ -537,7 +543,7 @@ moe_status_t moe_dispatch(const int32_t* idx, int T, int N, int K, int32_t* coun
   if (workspace_bytes < dispatch_ws_bytes(T, N, K))
     return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_dispatch_workspace_size()");
   char* ws = (char*)workspace;
-  const size_t nt = (size_t)rank_tiles(T);
+  const size_t nt = (size_t)moe::rank_row(rank_tiles(T));
   int32_t* rank = (int32_t*)ws;
   int32_t* tile_counts = (int32_t*)(ws + align256((size_t)T * K * 4));
   int32_t* tile_base = (int32_t*)((char*)tile_counts + align256(nt * N * 4));
@@ -652,7 +658,7 @@ BwdLayout make_bwd_layout(int T, int d, int I, int N, int K, int K_s, int dtype)
     o = align256(o + bytes);
     return at;
   };
-  const size_t TK = (size_t)T * K, es = elem_size(dtype), nt = (size_t)rank_tiles(T);
+  const size_t TK = (size_t)T * K, es = elem_size(dtype), nt = (size_t)moe::rank_row(rank_tiles(T));
   L.pipe = bwd_pipe(dtype);
   const size_t gen = L.pipe ? 0 : 1;  // buffers only the generic path uses
   L.idx = take(TK * 4);

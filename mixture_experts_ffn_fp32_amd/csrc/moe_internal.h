@@ -89,10 +89,15 @@ __device__ __forceinline__ int lds_chunk_offset_t(int r, int c) {
 }
 
 // ---------------------------------------------------------------- launchers
-// Router: logits, softmax, top-K.  Returns hipError_t of the launch.
+// Router: logits, softmax, top-K.  Returns hipError_t of the launch.  With
+// `rank` and `tile_counts` set, the tiled router (batches of more than 128
+// tokens, or any batch with MOE_ROUTER_SMALL=0) also writes step 1 of the
+// dispatch for its kRankTile-token blocks (what tile_rank below writes) and
+// sets *ranked; the one-block-per-token router leaves *ranked false.
 hipError_t launch_router(int dtype, const void* u, const void* E_gate, const float* bias, int T,
                          int d, int N, int K, int32_t* idx, float* gate, float* scores,
-                         hipStream_t stream);
+                         hipStream_t stream, int32_t* rank = nullptr,
+                         int32_t* tile_counts = nullptr, bool* ranked = nullptr);
 
 // Tile tables of the grouped GEMMs: per virtual expert (routed experts, then
 // the shared ones) an exclusive prefix of m-tiles of bm rows, and the
@@ -142,8 +147,14 @@ __device__ __forceinline__ void tile_tables_wave(const int* off, int N, int TK,
   }
 }
 
-// Dispatch: per-64-token tile ranks, global scan, scatter.
-constexpr int kRankTile = 64;
+// Dispatch: per-tile ranks (tiles of kRankTile tokens, the tiled router's
+// block), global scan, scatter; batches of at most kSmallDispatchT tokens in
+// one launch.
+constexpr int kRankTile = 32;
+constexpr int kSmallDispatchT = 64;
+// tile_counts and tile_base are [N][rank_row(ntiles)]: one row of tiles per
+// expert, its length rounded up to whole 16-byte groups.
+__host__ __device__ inline int rank_row(int ntiles) { return (ntiles + 3) & ~3; }
 hipError_t launch_tile_rank(const int32_t* idx, int T, int N, int K, int32_t* tile_counts,
                             int32_t* rank, hipStream_t stream);
 // tt.tiles1 == NULL: no tile tables.

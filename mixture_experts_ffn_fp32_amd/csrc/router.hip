@@ -92,17 +92,22 @@ __global__ __launch_bounds__(512) void router_kernel(const typename E::T* __rest
                                                      const float* __restrict__ bias, int T, int d,
                                                      int N, int K, int32_t* __restrict__ idx,
                                                      float* __restrict__ gate,
-                                                     float* __restrict__ scores) {
+                                                     float* __restrict__ scores,
+                                                     int32_t* __restrict__ rank,
+                                                     int32_t* __restrict__ tile_counts) {
   using Tp = typename E::T;
   using C = RouterCfg<E, F, CH>;
   constexpr int TB = kRouterTB, NP = C::NP, FW = F / 2, NI = C::NI, S = C::S;
   constexpr int SLOT = C::SLOT;
   constexpr int kStep = CH * E::kPerChunk;  // contraction elements per stage
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SLOT];
+  __shared__ uint32_t s_mask[NP];  // dispatch ranks: the block's tokens per expert, one bit each
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
+  static_assert(TB == kRankTile && TB <= 32, "a rank tile is one block, one mask bit per token");
+  if (rank != nullptr && tid < NP) s_mask[tid] = 0u;  // ordered before use by the barriers below
   const int nsteps = d / kStep;
   // the stages are taken in an order rotated per block (stage g reads
   // contraction slice (g + rot) mod nsteps): every block reads all of E_gate,
@@ -180,8 +185,11 @@ __global__ __launch_bounds__(512) void router_kernel(const typename E::T* __rest
 
   // acc[f][r]: token tg*16 + 4*(lane/16) + r, expert (fh*FW + f)*16 + lane%16.
   constexpr int LP = NP + 1;  // padded logit row (floats)
-  static_assert(TB * LP * 4 <= S * SLOT, "logits fit the ring");
+  static_assert(((TB * LP * 4 + 255) & ~255) + TB * NP * 4 <= S * SLOT,
+                "logits and selections fit the ring");
   float* lg = (float*)ring;
+  // each token's selected experts in order (dispatch ranks), after the logits
+  int* sel = (int*)(ring + ((TB * LP * 4 + 255) & ~255));
   __syncthreads();  // every wavefront's last reads of the ring are done
   if (wave < 4) {
 #pragma unroll
@@ -253,9 +261,34 @@ __global__ __launch_bounds__(512) void router_kernel(const typename E::T* __rest
       if (col == 0 && t < T) {
         idx[(size_t)t * K + k] = bi;
         gate[(size_t)t * K + k] = bv;
+        if (rank != nullptr) {
+          sel[tl * K + k] = bi;
+          // (no expert: scores that are all NaN; the dispatch ignores such ids)
+          if ((unsigned)bi < (unsigned)N) atomicOr(&s_mask[bi], 1u << tl);
+        }
       }
     }
   }
+  if (rank == nullptr) return;
+  // Dispatch step 1 for this tile of TB tokens (the block): the rank of each
+  // pair among the tile's pairs of the same expert, in token order (the
+  // number of the tile's lower tokens that selected it), and each expert's
+  // count in the tile.
+  __syncthreads();
+  {
+    const int tl = wave * 4 + grp;
+    const int t = t0 + tl;
+    if (t < T) {
+      const uint32_t below = (1u << tl) - 1u;
+      for (int k = col; k < K; k += 16) {
+        const int e = sel[tl * K + k];
+        rank[(size_t)t * K + k] = (unsigned)e < (unsigned)N ? __popc(s_mask[e] & below) : 0;
+      }
+    }
+  }
+  const int row = rank_row((int)gridDim.x);
+  for (int e = tid; e < N; e += blockDim.x)
+    tile_counts[(size_t)e * row + blockIdx.x] = __popc(s_mask[e]);
 }
 
 // Small batches (decode): one block per token.  Each of the 256 threads takes
@@ -446,7 +479,8 @@ __global__ __launch_bounds__(256) void router_small_kernel(const typename E::T* 
 // The widest stage the row length allows (fewer, longer stages for few experts).
 template <class E, int F>
 hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int T, int d, int N,
-                           int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
+                           int K, int32_t* idx, float* gate, float* scores, int32_t* rank,
+                           int32_t* tile_counts, hipStream_t st) {
   using Tp = typename E::T;
   const dim3 grid((T + kRouterTB - 1) / kRouterTB), block(512);
   const Tp* up = (const Tp*)u;
@@ -455,9 +489,9 @@ hipError_t launch_router_f(const void* u, const void* Eg, const float* bias, int
   constexpr int CHW = F <= 4 ? 32 : F == 8 ? 16 : 8;  // chunks per stage the LDS ring holds
   if (row % (CHW * 16) == 0)
     return launch_kernel(router_kernel<E, F, CHW>, grid, block, st, up, ep, bias, T, d, N, K, idx,
-                         gate, scores);
+                         gate, scores, rank, tile_counts);
   return launch_kernel(router_kernel<E, F, 8>, grid, block, st, up, ep, bias, T, d, N, K, idx, gate,
-                       scores);
+                       scores, rank, tile_counts);
 }
 
 // Batches of at most kSmallRouterMaxT tokens take the one-block-per-token
@@ -469,26 +503,35 @@ bool router_small() {
 
 template <class E>
 hipError_t launch_router_t(const void* u, const void* Eg, const float* bias, int T, int d, int N,
-                           int K, int32_t* idx, float* gate, float* scores, hipStream_t st) {
+                           int K, int32_t* idx, float* gate, float* scores, int32_t* rank,
+                           int32_t* tile_counts, bool* ranked, hipStream_t st) {
   using Tp = typename E::T;
+  if (ranked != nullptr) *ranked = false;
   if (T <= kSmallRouterMaxT && router_small()) {
     return launch_kernel(router_small_kernel<E>, dim3(T), dim3(256), st, (const Tp*)u,
                          (const Tp*)Eg, bias, T, d, N, K, idx, gate, scores);
   }
-  if (N <= 32) return launch_router_f<E, 2>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
-  if (N <= 64) return launch_router_f<E, 4>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
-  if (N <= 128) return launch_router_f<E, 8>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
-  return launch_router_f<E, 16>(u, Eg, bias, T, d, N, K, idx, gate, scores, st);
+  if (rank == nullptr || tile_counts == nullptr) rank = tile_counts = nullptr;
+  if (ranked != nullptr) *ranked = rank != nullptr;
+  if (N <= 32)
+    return launch_router_f<E, 2>(u, Eg, bias, T, d, N, K, idx, gate, scores, rank, tile_counts, st);
+  if (N <= 64)
+    return launch_router_f<E, 4>(u, Eg, bias, T, d, N, K, idx, gate, scores, rank, tile_counts, st);
+  if (N <= 128)
+    return launch_router_f<E, 8>(u, Eg, bias, T, d, N, K, idx, gate, scores, rank, tile_counts, st);
+  return launch_router_f<E, 16>(u, Eg, bias, T, d, N, K, idx, gate, scores, rank, tile_counts, st);
 }
 
 }  // namespace
 
 hipError_t launch_router(int dtype, const void* u, const void* E_gate, const float* bias, int T,
                          int d, int N, int K, int32_t* idx, float* gate, float* scores,
-                         hipStream_t stream) {
+                         hipStream_t stream, int32_t* rank, int32_t* tile_counts, bool* ranked) {
   if (dtype == 1)
-    return launch_router_t<ElemBF16>(u, E_gate, bias, T, d, N, K, idx, gate, scores, stream);
-  return launch_router_t<ElemF32>(u, E_gate, bias, T, d, N, K, idx, gate, scores, stream);
+    return launch_router_t<ElemBF16>(u, E_gate, bias, T, d, N, K, idx, gate, scores, rank,
+                                     tile_counts, ranked, stream);
+  return launch_router_t<ElemF32>(u, E_gate, bias, T, d, N, K, idx, gate, scores, rank,
+                                  tile_counts, ranked, stream);
 }
 
 }  // namespace moe

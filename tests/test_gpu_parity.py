@@ -266,8 +266,11 @@ def test_stage_timing_covers_every_launched_stage(name):
     torch.cuda.synchronize()
     mx.timing_enable(False)
     st = mx.timing_read()
-    small_batch = w.T <= 64
-    expect = {"router", "expert_gemm1_swiglu", "expert_gemm2_down", "combine", "tile_rank"}
+    small_batch = w.T <= 64      # one dispatch launch (timed as tile_rank)
+    tiled_router = w.T > 128     # the router also writes the dispatch ranks
+    expect = {"router", "expert_gemm1_swiglu", "expert_gemm2_down", "combine"}
+    if small_batch or not tiled_router:
+        expect.add("tile_rank")
     if not small_batch:
         expect |= {"dispatch_scan", "scatter"}
     for name_, (ms, n) in st.items():
