@@ -111,9 +111,12 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   const int row = rank_row(ntiles), nq = row / 4;  // 16-byte groups per row
   const int rounds = (nq + G - 1) / G;
   const u32x4* src = (const u32x4*)(tile_counts + (size_t)(live ? e : 0) * row);
-  // group q of the row, the counts past the last tile (row padding) as 0
+  // group q of the row, the counts past the last tile (row padding, and
+  // groups past the row) as 0.  The load itself is unconditional (an
+  // in-range group): a load under a lane-dependent branch would be waited
+  // for before the branch joins, one round trip per group.
   auto group = [&](int q) {
-    u32x4 v = q < nq ? src[q] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 v = src[min(q, nq - 1)];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (4 * q + j >= ntiles) v[j] = 0u;
@@ -125,20 +128,20 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   const bool in_regs = rounds <= R;
   u32x4 cr[R];
   int s = 0;
-  if (live) {
-    if (in_regs) {
+  // (lanes of experts past N read row 0 and their sums go unused)
+  if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) cr[i] = i < rounds ? group(i * G + g) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < R; ++i) cr[i] = group(i * G + g);
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first is used
 #pragma unroll
-      for (int i = 0; i < R; ++i) s += sum4(cr[i]);
-    } else {
-      for (int i0 = 0; i0 < rounds; i0 += R) {
-        u32x4 c[R];
+    for (int i = 0; i < R; ++i) s += sum4(cr[i]);
+  } else {
+    for (int i0 = 0; i0 < rounds; i0 += R) {
+      u32x4 c[R];
 #pragma unroll
-        for (int i = 0; i < R; ++i) c[i] = i0 + i < rounds ? group((i0 + i) * G + g) : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < R; ++i) c[i] = group((i0 + i) * G + g);
 #pragma unroll
-        for (int i = 0; i < R; ++i) s += sum4(c[i]);
-      }
+      for (int i = 0; i < R; ++i) s += sum4(c[i]);
     }
   }
   // the expert's total: the last lane of its segment
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     for (int i = 0; i < R; ++i)
       if (i < rounds) round_bases(i * G + g, cr[i]);
   } else {
-    for (int i = 0; i < rounds; ++i) round_bases(i * G + g, live ? group(i * G + g) : u32x4{0u, 0u, 0u, 0u});
+    for (int i = 0; i < rounds; ++i) round_bases(i * G + g, group(i * G + g));
   }
 }
 
