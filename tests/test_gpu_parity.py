@@ -248,6 +248,31 @@ def test_layer_forward_short_run_streaming(name, monkeypatch):
             w.name)
 
 
+@pytest.mark.parametrize("name", ["decode_n256_bf16", "k_equals_n_f32", "one_token_bf16"])
+def test_layer_forward_tiled_router_small_batch(name, monkeypatch):
+    """MOE_ROUTER_SMALL=0 sends batches of at most 128 tokens to the tiled router, which
+    then also writes the dispatch ranks of its 32-token blocks when the batch has more
+    than 64 tokens (T = 96 and 70 here; T = 1 keeps the one-launch dispatch): the layer
+    must match the oracle on that path as well."""
+    up = Uploaded(small_inputs(name))
+    w = up.w
+    say(f"layer_forward MOE_ROUTER_SMALL=0 {w.name}")
+    monkeypatch.setenv("MOE_ROUTER_SMALL", "0")
+    h = mx.layer_forward(up.u, up.E, up.W_routed, up.W_shared, w.N, w.K, w.K_s, up.bias)
+    idx, gate, _ = mx.route(up.u, up.E, w.K, up.bias)
+    torch.cuda.synchronize()
+    inp = up.inp
+    h_ref, info = oracle.moe_forward_tokens(inp.u_f32(), inp.E_gate_f32(), up.routed, up.shared,
+                                            w.N, w.K, w.K_s, inp.gate_bias())
+    differing, alts = check_routing(idx.cpu().numpy(), gate.cpu().numpy(), info["s"], w.K)
+    for t in differing:
+        a_idx, a_g = alts[int(t)]
+        h_ref[t] = oracle.moe_forward_given_routing(inp.u_f32()[t:t + 1], a_idx[None], a_g[None],
+                                                    up.routed, up.shared, w.K_s)[0]
+    check_h(device_f32(h), h_ref, inp.u_f32().astype(np.float64), tol_for(w), w.dtype, w.K,
+            w.name)
+
+
 @pytest.mark.parametrize("name", ["pp_ragged_bf16", "decode_n256_bf16", "one_token_bf16"])
 def test_stage_timing_covers_every_launched_stage(name):
     """Timing on: every stage the forward launches reports one launch per call with a
