@@ -15,40 +15,11 @@
 //     offsets (exclusive scan over experts) and per-(tile, expert) bases.
 //  3. scatter: sorted_pair[base + rank] = p.
 // A batch of at most 64 tokens (decode) does all three in one launch.
+#include "dispatch_wave.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
-// Expert ids of token t's K pairs, all requested before any is used (up to
-// kKReg of them in registers; more are read again where needed).
-constexpr int kKReg = 16;
-__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int t, int K,
-                                         int (&ev)[kKReg]) {
-#pragma unroll
-  for (int k = 0; k < kKReg; ++k)
-    if (k < K) ev[k] = idx[(size_t)t * K + k];
-}
-// f(k, e) for each of token t's pairs in order k = 0 .. K-1 (register
-// indices fixed at compile time, so the ids stay in registers).
-template <class F>
-__device__ __forceinline__ void for_ids(const int32_t* __restrict__ idx, int t, int K,
-                                        const int (&ev)[kKReg], F f) {
-#pragma unroll
-  for (int k = 0; k < kKReg; ++k)
-    if (k < K) f(k, ev[k]);
-  for (int k = kKReg; k < K; ++k) f(k, idx[(size_t)t * K + k]);
-}
 
 // One wavefront per tile of kRankTile tokens; lane = token (lanes past the
 // tile idle).
@@ -208,8 +179,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }
 
 // A batch of at most 64 tokens in one launch (one wavefront, lane = token):
-// the lane masks of step 1 for the single tile, then the expert counts, their
-// exclusive scan and the scatter -- the same ranks and order as steps 1-3.
+// the ranks, counts, offsets and sorted pairs of dispatch_wave, and the tile
+// tables -- the same ranks and order as steps 1-3.
 __global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __restrict__ idx,
                                                             int T, int N, int K,
                                                             int32_t* __restrict__ counts,
@@ -218,42 +189,8 @@ __global__ __launch_bounds__(64) void dispatch_small_kernel(const int32_t* __res
                                                             TileTableOut tt) {
   __shared__ unsigned long long mask[256];
   __shared__ int s_off[257];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < N; e += 64) mask[e] = 0ull;
-  __syncthreads();
-  const unsigned long long bit = 1ull << lane;
-  int ev[kKReg];
-  if (lane < T) load_ids(idx, lane, K, ev);
-  if (lane < T)
-    for_ids(idx, lane, K, ev, [&](int, int e) {
-      if ((unsigned)e < (unsigned)N) atomicOr(&mask[e], bit);
-    });
-  __syncthreads();
-  int carry = 0;
-  for (int b = 0; b < N; b += 64) {
-    const int e = b + lane;
-    const int c = e < N ? __popcll(mask[e]) : 0;
-    const int inc = wave_inclusive_scan(c);
-    if (e < N) {
-      counts[e] = c;
-      s_off[e] = carry + inc - c;
-      offsets[e] = carry + inc - c;
-    }
-    carry += __shfl(inc, 63);
-  }
-  if (lane == 0) {
-    offsets[N] = carry;
-    s_off[N] = carry;
-  }
-  __syncthreads();
-  if (tt.tiles1 != nullptr) tile_tables_wave(s_off, N, carry, tt);
-  if (lane < T) {
-    const unsigned long long below = bit - 1ull;
-    for_ids(idx, lane, K, ev, [&](int k, int e) {
-      if ((unsigned)e < (unsigned)N)
-        sorted_pair[s_off[e] + __popcll(mask[e] & below)] = lane * K + k;
-    });
-  }
+  dispatch_wave(idx, T, N, K, mask, s_off, nullptr, counts, offsets, sorted_pair);
+  if (tt.tiles1 != nullptr) tile_tables_wave(s_off, N, s_off[N], tt);
 }
 
 }  // namespace

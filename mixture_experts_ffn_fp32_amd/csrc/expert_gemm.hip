@@ -1155,6 +1155,11 @@ hipError_t launch_mode(const ExpertArgs& a, hipStream_t st) {
 
 }  // namespace
 
+bool gemm1_derives_dispatch(int dtype, const ExpertArgs& a) {
+  return dtype == 1 && a.T <= kSmallDispatchT && (long long)a.T * a.K <= kFusedDispatchPairs &&
+         shape1(a, 2).kind == 3;
+}
+
 int expert_tile_table_ints(int N, int K_s) { return (N + K_s + 1) + (N + 2) + 16; }
 
 TileTableOut expert_tile_tables(int dtype, const ExpertArgs& a) {

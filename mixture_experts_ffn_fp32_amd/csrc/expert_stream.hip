@@ -28,6 +28,7 @@
 //    columns of one token), each on half of every k-step's k-groups; the
 //    second hands its sums to the first through LDS, which finishes the tile
 //    with 8-byte stores.
+#include "dispatch_wave.h"
 #include "lds_dma.h"
 #include "moe_internal.h"
 
@@ -105,12 +106,30 @@ __global__ __launch_bounds__(kSlThreads, 1) void expert_stream_long_kernel(Exper
   __shared__ __attribute__((aligned(16))) f32x4 xbuf[2][2][64];  // second wavefront's partial sums
   __shared__ int s_tab[kSlMaxV + 1];
   __shared__ int s_off[kSlMaxV + 1];
+  __shared__ int s_sp[MODE == 1 ? kFusedDispatchPairs : 1];  // sorted pairs derived here
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = MODE == 1 ? a.N + a.K_s : a.N + (a.K_s > 0 ? 1 : 0);
   const int32_t* tab = MODE == 1 ? a.tiles1 : a.tiles2;
-  for (int i = tid; i <= V; i += blockDim.x) s_tab[i] = tab[i];
-  for (int i = tid; i <= a.N; i += blockDim.x) s_off[i] = a.offsets[i];
+  // GEMM1 of a decode batch may derive the dispatch itself (the routing in
+  // fd.idx): one wavefront of every block computes the offsets, the sorted
+  // pairs and this launch's tile table into LDS (the lane masks in the token-
+  // row region, free until the first segment); block 0 also writes them out,
+  // with the tile tables, for the GEMM2 and combine launches.
+  const bool derived = MODE == 1 && a.fd.idx != nullptr;
+  if (derived) {
+    if (wave == 0) {
+      const bool b0 = blockIdx.x == 0;
+      dispatch_wave(a.fd.idx, a.T, a.N, a.K, (unsigned long long*)areg, s_off, s_sp,
+                    b0 ? a.fd.counts : nullptr, b0 ? a.fd.offsets : nullptr,
+                    b0 ? a.fd.sorted_pair : nullptr);
+      if (b0 && a.fd.tt.tiles1 != nullptr) tile_tables_wave(s_off, a.N, s_off[a.N], a.fd.tt);
+      mtile_prefix_wave(s_off, a.N, V, a.T, a.T * a.K, kSlBM, s_tab);
+    }
+  } else {
+    for (int i = tid; i <= V; i += blockDim.x) s_tab[i] = tab[i];
+    for (int i = tid; i <= a.N; i += blockDim.x) s_off[i] = a.offsets[i];
+  }
   __syncthreads();
 
   // The block's work: with at least as many segments as blocks, a
@@ -240,7 +259,7 @@ __global__ __launch_bounds__(kSlThreads, 1) void expert_stream_long_kernel(Exper
         if (MODE == 1) {
           src_row = p;
           if (v < a.N) {
-            const int pair = a.sorted_pair[row_base + p];
+            const int pair = derived ? s_sp[row_base + p] : a.sorted_pair[row_base + p];
             src_row = ((unsigned)pair < (unsigned)TK) ? pair / a.K : 0;
           }
         } else {

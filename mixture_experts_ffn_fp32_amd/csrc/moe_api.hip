@@ -394,10 +394,18 @@ moe_status_t forward_enqueue(const void* u, const void* E_gate, const void* W_ro
       return hip_fail(e, "router launch");
   }
   const moe::TileTableOut tables = moe::expert_tile_tables(dtype, ar);
-  if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
-                        (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
-                        (int32_t*)(ws + L.tile_base), st, &tables, rec, ranked)) != MOE_OK)
+  if (moe::gemm1_derives_dispatch(dtype, ar)) {
+    // a decode batch: GEMM1 derives the dispatch itself, in every block
+    ar.fd.idx = idx;
+    ar.fd.counts = (int32_t*)(ws + L.counts);
+    ar.fd.offsets = offsets;
+    ar.fd.sorted_pair = sorted_pair;
+    ar.fd.tt = tables;
+  } else if ((s = run_dispatch(idx, T, N, K, (int32_t*)(ws + L.counts), offsets, sorted_pair,
+                               (int32_t*)(ws + L.rank), (int32_t*)(ws + L.tile_counts),
+                               (int32_t*)(ws + L.tile_base), st, &tables, rec, ranked)) != MOE_OK) {
     return s;
+  }
   if ((s = run_experts(dtype, ar, st, true, rec)) != MOE_OK) return s;
   if (side && (e = hipStreamWaitEvent(st, sd->join, 0)) != hipSuccess)
     return hip_fail(e, "shared-expert join");

@@ -186,7 +186,24 @@ struct ExpertArgs {
   // N that picks the kernels (0: N).  A launch over the shared experts alone
   // (N = 0) keeps the choice the whole layer would make.
   int sel_N;
+  // A decode batch's dispatch derived inside GEMM1 (idx set; only where
+  // gemm1_derives_dispatch says so): every block computes it from the
+  // routing, block 0 also writes its outputs and the tile tables for the
+  // launches after it.
+  struct {
+    const int32_t* idx;     // [T][K]
+    int32_t* counts;        // [N]
+    int32_t* offsets;       // [N+1] (the array `offsets` above then points to)
+    int32_t* sorted_pair;   // [T*K] (likewise)
+    TileTableOut tt;
+  } fd;
 };
+// Most (token, expert) pairs a GEMM1 launch derives the dispatch of itself.
+constexpr int kFusedDispatchPairs = 1024;
+// Whether the GEMM1 launch of these shapes derives the dispatch itself when
+// given the routing (a bf16 batch of at most kSmallDispatchT tokens on the
+// long-run streaming kernel, at most kFusedDispatchPairs pairs).
+bool gemm1_derives_dispatch(int dtype, const ExpertArgs& a);
 // Weight streaming with 512-byte runs per weight row (expert_stream.hip):
 // whether a launch of GEMM `mode` fits it, its m-tile height, and the launch.
 bool stream_long_ok(int mode, const ExpertArgs& a);

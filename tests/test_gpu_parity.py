@@ -291,10 +291,13 @@ def test_stage_timing_covers_every_launched_stage(name):
     torch.cuda.synchronize()
     mx.timing_enable(False)
     st = mx.timing_read()
-    small_batch = w.T <= 64      # one dispatch launch (timed as tile_rank)
+    small_batch = w.T <= 64      # one dispatch launch (timed as tile_rank) ...
+    # ... unless GEMM1 derives the dispatch itself (a bf16 decode batch on the
+    # long-run streaming kernel, as these small shapes are)
+    derived = small_batch and w.dtype == "bf16" and w.T * w.K <= 1024
     tiled_router = w.T > 128     # the router also writes the dispatch ranks
     expect = {"router", "expert_gemm1_swiglu", "expert_gemm2_down", "combine"}
-    if small_batch or not tiled_router:
+    if (small_batch and not derived) or (not small_batch and not tiled_router):
         expect.add("tile_rank")
     if not small_batch:
         expect |= {"dispatch_scan", "scatter"}
