@@ -15,6 +15,8 @@
 //     offsets (exclusive scan over experts) and per-(tile, expert) bases.
 //  3. scatter: sorted_pair[base + rank] = p.
 // A batch of at most 64 tokens (decode) does all three in one launch.
+#include <algorithm>
+
 #include "dispatch_wave.h"
 #include "moe_internal.h"
 
@@ -178,6 +180,108 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   sorted_pair[tile_base[(size_t)e * row + t / kRankTile] + rank[p]] = (int32_t)p;
 }
 
+// Steps 2 and 3 in one launch, for batches whose tile counts are small
+// enough to read whole in every block (N * rank_row(ntiles) <= kScanScatterMax
+// ints): block b owns RT consecutive tiles.  Each block derives what its
+// scatter needs from the counts — every expert's total and its count in the
+// tiles before the block's own (thread (e, g) sums groups g, g + P, ... of
+// expert e's row, P threads per expert), the totals' exclusive scan (the
+// offsets) and the bases of its own tiles — then writes the sorted pairs of
+// its tokens.  Block 0 also writes counts, offsets and the tile tables.
+constexpr int kScanScatterRT = 16;           // most tiles per block
+constexpr int kScanScatterMax = 16 * 1024;   // most tile counts a block reads (64 KB)
+
+__global__ __launch_bounds__(256) void scan_scatter_kernel(const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ rank,
+                                                           const int32_t* __restrict__ tile_counts,
+                                                           int T, int N, int K, int NP2, int ntiles,
+                                                           int RT, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_pair,
+                                                           TileTableOut tt) {
+  __shared__ int s_tot[256], s_below[256], s_off[257];
+  __shared__ int s_base[kScanScatterRT][256];  // the block's tiles: counts, then bases
+  const int tid = threadIdx.x;
+  const int P = min(max(256 / NP2, 1), 64);  // threads per expert (one wavefront at most)
+  const int e = tid / P, g = tid % P;
+  const bool live = e < N;
+  const int row = rank_row(ntiles), nq = row / 4;
+  const int j0 = blockIdx.x * RT, j1 = min(j0 + RT, ntiles);
+  const u32x4* src = (const u32x4*)(tile_counts + (size_t)(live ? e : 0) * row);
+  // group q's counts: the total, the part before tile j0, the block's own
+  int tot = 0, below = 0;
+  auto take = [&](int q, u32x4 c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * q + i;
+      const int v = j < ntiles ? (int)c[i] : 0;  // (row padding)
+      tot += v;
+      if (j < j0) below += v;
+      else if (j < j1 && live) s_base[j - j0][e] = v;
+    }
+  };
+  constexpr int B = 16;
+  for (int q0 = g; q0 < nq; q0 += B * P) {
+    u32x4 c[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) c[i] = src[min(q0 + i * P, nq - 1)];  // unconditional, in range
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+      if (q0 + i * P < nq) take(q0 + i * P, c[i]);
+  }
+  // the P partial sums of an expert (consecutive lanes)
+  for (int o = 1; o < P; o <<= 1) {
+    tot += __shfl_xor(tot, o, P);
+    below += __shfl_xor(below, o, P);
+  }
+  if (live && g == 0) {
+    s_tot[e] = tot;
+    s_below[e] = below;
+  }
+  __syncthreads();
+  // exclusive scan of the totals over experts (first wavefront, 64 at a time)
+  if (tid < 64) {
+    int carry = 0;
+    for (int b = 0; b < N; b += 64) {
+      const int v = (b + tid < N) ? s_tot[b + tid] : 0;
+      const int incv = wave_inclusive_scan(v);
+      const int total = __shfl(incv, 63);
+      if (b + tid < N) {
+        s_off[b + tid] = carry + incv - v;
+        if (blockIdx.x == 0) {
+          counts[b + tid] = v;
+          offsets[b + tid] = carry + incv - v;
+        }
+      }
+      carry += total;
+    }
+    if (tid == 0) {
+      s_off[N] = carry;
+      if (blockIdx.x == 0) offsets[N] = carry;
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid < 64 && tt.tiles1 != nullptr) tile_tables_wave(s_off, N, s_off[N], tt);
+  // the bases of the block's tiles
+  for (int x = tid; x < N; x += 256) {
+    int run = s_off[x] + s_below[x];
+    for (int r = 0; r < j1 - j0; ++r) {
+      const int c = s_base[r][x];
+      s_base[r][x] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const long long p0 = (long long)j0 * kRankTile * K;
+  const long long p1 = (long long)min(j1 * kRankTile, T) * K;
+  for (long long p = p0 + tid; p < p1; p += 256) {
+    const int t = (int)(p / K);
+    const int x = idx[p];
+    if ((unsigned)x >= (unsigned)N) continue;
+    sorted_pair[s_base[t / kRankTile - j0][x] + rank[p]] = (int32_t)p;
+  }
+}
+
 // A batch of at most 64 tokens in one launch (one wavefront, lane = token):
 // the ranks, counts, offsets and sorted pairs of dispatch_wave, and the tile
 // tables -- the same ranks and order as steps 1-3.
@@ -216,6 +320,26 @@ hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, i
   while (np2 < N) np2 <<= 1;
   return launch_kernel(dispatch_scan_kernel, dim3(1), dim3(1024), stream, tile_counts, ntiles, N,
                        np2, counts, offsets, tile_base, tt);
+}
+
+bool scan_scatter_fits(int T, int N) {
+  const int ntiles = (T + kRankTile - 1) / kRankTile;
+  int np2 = 1;
+  while (np2 < N) np2 <<= 1;
+  const int RT = std::max(2, (ntiles + 127) / 128);
+  return RT <= kScanScatterRT && (long long)N * rank_row(ntiles) <= kScanScatterMax;
+}
+
+hipError_t launch_scan_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_counts,
+                               int T, int N, int K, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_pair, const TileTableOut& tt, hipStream_t stream) {
+  const int ntiles = (T + kRankTile - 1) / kRankTile;
+  int np2 = 1;
+  while (np2 < N) np2 <<= 1;
+  const int RT = std::max(2, (ntiles + 127) / 128);  // about 128 blocks
+  const int blocks = (ntiles + RT - 1) / RT;
+  return launch_kernel(scan_scatter_kernel, dim3(blocks), dim3(256), stream, idx, rank, tile_counts,
+                       T, N, K, np2, ntiles, RT, counts, offsets, sorted_pair, tt);
 }
 
 hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_base,

@@ -271,6 +271,13 @@ moe_status_t run_dispatch(const int32_t* idx, int T, int N, int K, int32_t* coun
     if ((e = moe::launch_tile_rank(idx, T, N, K, tile_counts, rank, st)) != hipSuccess)
       return hip_fail(e, "tile rank launch");
   }
+  if (moe::scan_scatter_fits(T, N)) {  // scan and scatter in one launch
+    StageScope sc(3, st, rec);
+    if ((e = moe::launch_scan_scatter(idx, rank, tile_counts, T, N, K, counts, offsets,
+                                      sorted_pair, tt, st)) != hipSuccess)
+      return hip_fail(e, "scan and scatter launch");
+    return MOE_OK;
+  }
   {
     StageScope sc(2, st, rec);
     if ((e = moe::launch_dispatch_scan(tile_counts, rank_tiles(T), N, counts, offsets, tile_base,

@@ -164,6 +164,12 @@ hipError_t launch_dispatch_scan(const int32_t* tile_counts, int ntiles, int N, i
 hipError_t launch_dispatch_small(const int32_t* idx, int T, int N, int K, int32_t* counts,
                                  int32_t* offsets, int32_t* sorted_pair, const TileTableOut& tt,
                                  hipStream_t stream);
+// Steps 2 and 3 in one launch (every block re-derives the scan it needs),
+// where the tile counts are small enough: scan_scatter_fits(T, N).
+bool scan_scatter_fits(int T, int N);
+hipError_t launch_scan_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_counts,
+                               int T, int N, int K, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_pair, const TileTableOut& tt, hipStream_t stream);
 hipError_t launch_scatter(const int32_t* idx, const int32_t* rank, const int32_t* tile_base,
                           int T, int N, int K, int32_t* sorted_pair, hipStream_t stream);
 
