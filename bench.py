@@ -9,7 +9,10 @@ The layer backward (all gradients, routing recomputed) is timed beside it.
 The default workload is the 16B-model-shaped prefill layer in bfloat16
 (T=8192 tokens, d=2048, 64 routed + 2 shared experts, top-6, intermediate
 1408).  The decode-shaped batch (T=64, same layer) is timed beside it.
-Prints one JSON line.
+Before each prefill workload's W warm-up and K timed steps, untimed forwards
+run for SETTLE_S seconds of GPU time (reported as "settle"): the inputs are
+generated on the host while the GPU idles, and its clocks need longer than a
+few steps to reach their level under this load.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -26,6 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (MFMA / vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+SETTLE_S = 0.25               # untimed forwards before each prefill timed pass (GPU time)
 
 
 def parse():
@@ -132,6 +136,34 @@ def time_layer(mx, t, w, steps, warmup, stage_timing, per_step_events=False):
     stages = mx.timing_read()
     per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)] if per_step_events else None
     return ev[0].elapsed_time(ev[steps]), per_step, stages
+
+
+def settle(mx, t, w, seconds):
+    """Untimed forwards for about `seconds` of GPU time before a timed pass: the inputs
+    were just generated on the host while the GPU idled, and its clocks take longer to
+    reach their level under this load than a few warm-up steps (a fixed time, not a step
+    count, so a short --warmup still times the steady state).  Returns the steps run."""
+    import torch
+
+    if seconds <= 0:
+        return 0
+    I = t["Wr"].numel() // (3 * w.N * w.d)
+    ws = torch.empty(mx.workspace_size(w.T, w.d, I, w.N, w.K, w.K_s, 1 if w.dtype == "bf16" else 0),
+                     dtype=torch.uint8, device=t["u"].device)
+    h = torch.empty_like(t["u"])
+    args = (t["u"], t["E"], t["Wr"], t["Ws"], w.N, w.K, w.K_s, t["bias"])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n, done, batch = 0, 0.0, 4
+    while done < seconds * 1e3:
+        e0.record()
+        for _ in range(batch):
+            mx.layer_forward(*args, out=h, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        done += e0.elapsed_time(e1)
+        n += batch
+        batch = min(batch * 2, 64)
+    return n
 
 
 def step_stats(per_step):
@@ -312,6 +344,7 @@ def other_workload(mx, name, steps, warmup, cpu_tokens):
     inp = moe_inputs.make(name)
     w = inp.w
     t = upload(inp, torch.device("cuda:0"))
+    settle(mx, t, w, SETTLE_S)
     ms, _, _ = time_layer(mx, t, w, steps, warmup, False)
     _, per_step, _ = time_layer(mx, t, w, steps, 1, False, per_step_events=True)
     _, _, stages = time_layer(mx, t, w, steps, 1, True)
@@ -356,6 +389,7 @@ def main():
     inp = moe_inputs.make(args.workload)
     w = inp.w
     t = upload(inp, dev)
+    settled = settle(mx, t, w, SETTLE_S)
     # the timed steps carry events around GEMM1 only (its launch duration for the
     # roofline); the per-stage breakdown comes from a second pass with every stage
     ms, _, g1_stage = time_layer(mx, t, w, args.steps, args.warmup, ["expert_gemm1_swiglu"])
@@ -426,7 +460,8 @@ def main():
     line = {
         "metric": "MoE-layer tokens/s (16B shape, bf16) + % bf16 MFMA peak / % HBM peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "settle": {"seconds": SETTLE_S, "steps": settled},
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "routed_experts": w.N, "top_k": w.K,
                    "shared_experts": w.K_s, "intermediate": w.I, "accumulate": "f32",
