@@ -188,6 +188,12 @@ SMALL = {
     # expert count, float32
     "decode_n256_bf16": dict(T=96, d=256, N=256, K=8, K_s=1, I=128, dtype="bf16", seed=1201),
     "decode_n200_f32": dict(T=100, d=192, N=200, K=5, K_s=0, I=64, dtype="f32", seed=1202),
+    # batches of at most 64 tokens: GEMM1 derives the dispatch itself (at most 1024
+    # pairs; 256 experts are four rounds of the wavefront's expert loop, two shared
+    # experts), and past 1024 pairs the one-launch dispatch (K = 20: ids past the 16
+    # held in registers)
+    "decode64_n256_bf16": dict(T=64, d=256, N=256, K=8, K_s=2, I=128, dtype="bf16", seed=1203),
+    "decode64_k20_bf16": dict(T=64, d=128, N=64, K=20, K_s=1, I=128, dtype="bf16", seed=1204),
 }
 
 
