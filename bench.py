@@ -286,6 +286,7 @@ def sweep(args):
              "Ws": (torch.randn(w.K_s * 3 * w.I * w.d, generator=g, device=dev, dtype=bf) * w.sigma
                     if w.K_s else None),
              "bias": None}
+        settle(mx, t, w, SETTLE_S)
         ms, _, _ = time_layer(mx, t, w, args.steps, args.warmup, False)
         _, per_step, _ = time_layer(mx, t, w, args.steps, 1, False, per_step_events=True)
         _, _, stages = time_layer(mx, t, w, args.steps, 1, True)
