@@ -194,6 +194,12 @@ SMALL = {
     # held in registers)
     "decode64_n256_bf16": dict(T=64, d=256, N=256, K=8, K_s=2, I=128, dtype="bf16", seed=1203),
     "decode64_k20_bf16": dict(T=64, d=128, N=64, K=20, K_s=1, I=128, dtype="bf16", seed=1204),
+    # decode batches with a model width that is not a multiple of 128 (six 32-column
+    # GEMM2 groups, the one-shared-expert GEMM2 on the long-run kernel) and with three
+    # shared experts (three shared virtual experts in GEMM1, GEMM2 on the short-run
+    # kernel)
+    "decode_d192_bf16": dict(T=40, d=192, N=24, K=3, K_s=1, I=192, dtype="bf16", seed=1205),
+    "decode_ks3_bf16": dict(T=48, d=128, N=32, K=4, K_s=3, I=64, dtype="bf16", seed=1206),
 }
 
 
