@@ -200,6 +200,9 @@ SMALL = {
     # kernel)
     "decode_d192_bf16": dict(T=40, d=192, N=24, K=3, K_s=1, I=192, dtype="bf16", seed=1205),
     "decode_ks3_bf16": dict(T=48, d=128, N=32, K=4, K_s=3, I=64, dtype="bf16", seed=1206),
+    # a decode GEMM2 neither streaming kernel takes (d = 320, two shared experts): the
+    # register-staged kernel in bf16
+    "decode_reg_bf16": dict(T=24, d=320, N=16, K=2, K_s=2, I=128, dtype="bf16", seed=1207),
 }
 
 
