@@ -368,7 +368,7 @@ def other_workload(mx, name, steps, warmup, cpu_tokens):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.profile_mode:
