@@ -203,6 +203,10 @@ SMALL = {
     # a decode GEMM2 neither streaming kernel takes (d = 320, two shared experts): the
     # register-staged kernel in bf16
     "decode_reg_bf16": dict(T=24, d=320, N=16, K=2, K_s=2, I=128, dtype="bf16", seed=1207),
+    # the two routers' boundary: 128 tokens (the last batch routed one block per token)
+    # and 129 (the tiled router, its last 32-token block holding one token)
+    "t128_bf16": dict(T=128, d=128, N=32, K=4, K_s=1, I=64, dtype="bf16", seed=1208),
+    "t129_f32": dict(T=129, d=64, N=8, K=2, K_s=1, I=64, dtype="f32", seed=1209),
 }
 
 
