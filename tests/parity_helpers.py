@@ -207,12 +207,21 @@ SMALL = {
     # and 129 (the tiled router, its last 32-token block holding one token)
     "t128_bf16": dict(T=128, d=128, N=32, K=4, K_s=1, I=64, dtype="bf16", seed=1208),
     "t129_f32": dict(T=129, d=64, N=8, K=2, K_s=1, I=64, dtype="f32", seed=1209),
+    # a wide model (d = 7168): token rows too long for the long-run streaming kernel
+    # (decode batch: the short-run kernels), 112 k-steps per pipelined GEMM1 tile; weights
+    # at sigma = 0.015 as the pages' widest layer (0.08 would give logits of std ~7, far
+    # from any trained router)
+    "wide_d_decode_bf16": dict(T=16, d=7168, N=8, K=2, K_s=1, I=256, dtype="bf16", seed=1210,
+                               sigma=0.015),
+    "wide_d_bf16": dict(T=300, d=7168, N=8, K=2, K_s=1, I=256, dtype="bf16", seed=1211,
+                        sigma=0.015),
 }
 
 
 def small_inputs(name):
     kw = dict(SMALL[name])
     seed = kw.pop("seed", None)
+    sigma = kw.pop("sigma", 0.08)
     if seed is None:
         seed = 1000 + sorted(k for k in SMALL if "seed" not in SMALL[k]).index(name)
-    return moe_inputs.custom(**kw, sigma=0.08, seed=seed, name=name)
+    return moe_inputs.custom(**kw, sigma=sigma, seed=seed, name=name)
