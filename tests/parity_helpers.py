@@ -215,6 +215,11 @@ SMALL = {
                                sigma=0.015),
     "wide_d_bf16": dict(T=300, d=7168, N=8, K=2, K_s=1, I=256, dtype="bf16", seed=1211,
                         sigma=0.015),
+    # the most shared experts the ABI takes (16), each I = 64: the pipelined GEMM2's
+    # shared tiles change W_down block at every k-step; the decode GEMM1 has 32 virtual
+    # experts
+    "ks16_bf16": dict(T=300, d=128, N=16, K=2, K_s=16, I=64, dtype="bf16", seed=1212),
+    "ks16_decode_bf16": dict(T=40, d=128, N=16, K=2, K_s=16, I=64, dtype="bf16", seed=1213),
 }
 
 
