@@ -220,6 +220,11 @@ SMALL = {
     # experts
     "ks16_bf16": dict(T=300, d=128, N=16, K=2, K_s=16, I=64, dtype="bf16", seed=1212),
     "ks16_decode_bf16": dict(T=40, d=128, N=16, K=2, K_s=16, I=64, dtype="bf16", seed=1213),
+    # every token to every routed expert (K = N = 32): in a decode batch exactly the 1024
+    # pairs GEMM1 derives the dispatch of itself; at 96 tokens the pipelined GEMMs
+    "k_equals_n_decode_bf16": dict(T=32, d=128, N=32, K=32, K_s=1, I=64, dtype="bf16",
+                                   seed=1214),
+    "k_equals_n_bf16": dict(T=96, d=128, N=32, K=32, K_s=0, I=64, dtype="bf16", seed=1215),
 }
 
 
