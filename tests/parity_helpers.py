@@ -225,6 +225,10 @@ SMALL = {
     "k_equals_n_decode_bf16": dict(T=32, d=128, N=32, K=32, K_s=1, I=64, dtype="bf16",
                                    seed=1214),
     "k_equals_n_bf16": dict(T=96, d=128, N=32, K=32, K_s=0, I=64, dtype="bf16", seed=1215),
+    # the narrowest model (d = 64) in bf16: one real k-step per GEMM1 tile (padded with a
+    # zero one), a GEMM2 n-tile a quarter full; and its decode batch on the long-run kernels
+    "d64_bf16": dict(T=600, d=64, N=4, K=2, K_s=1, I=64, dtype="bf16", seed=1216),
+    "d64_decode_bf16": dict(T=100, d=64, N=8, K=2, K_s=1, I=64, dtype="bf16", seed=1217),
 }
 
 
